@@ -1,0 +1,219 @@
+"""Benchmark: absorbed MLA decode on one MI355X.
+
+One step = the whole absorbed path over one batch of the DeepSeek-V3-shaped
+decode workload (B=64 sequences, H=128 heads, 4096 cached rows each in a
+contiguous bf16 latent cache [64, 4096, 576], one query token, seeded Gaussian
+inputs): absorb W_UK into the queries, scan the latent cache (split-T), merge
+the splits, project back through W_UV.  Inputs are resident in HBM before the
+timed region; each step reads a different one of three cache copies so the
+256 MB last-level cache cannot serve a step from the previous one.
+
+Prints one JSON line.  ``value`` is the step's algorithmic TFLOP/s; the line
+also carries the algorithmic HBM GB/s, tokens/s, the roofline of the dominant
+kernel (the split-T latent scan, timed with HIP events on the stream it runs
+on) and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+N_COPIES = 3
+
+
+def algorithmic_counts(B, s_q, H, seqlens, causal, cache_elem_bytes=2, scale_bytes=0):
+    """FLOPs and bytes by the pages' counting rule: 2 per multiply-add over the
+    causally visible (query, cached row) pairs, 2*576 + 2*512 per head and pair;
+    a cached row is read once."""
+    pairs = 0
+    rows = 0
+    for T in seqlens:
+        rows += T
+        for j in range(s_q):
+            pairs += (T - s_q + j + 1) if causal else T
+    f_scan = pairs * H * (2 * 576 + 2 * 512)
+    f_absorb = 2 * (2 * B * s_q * H * 128 * 512)
+    by_cache = rows * (576 * cache_elem_bytes + scale_bytes)
+    by_qlat = B * s_q * H * 576 * 2
+    by_weights = 2 * H * 128 * 512 * 2
+    by_q, by_out = B * s_q * H * 192 * 2, B * s_q * H * 128 * 2
+    return dict(flops_scan=f_scan, flops_step=f_scan + f_absorb,
+                bytes_scan=by_cache + by_qlat,
+                bytes_step=by_cache + by_weights + by_q + by_out)
+
+
+def cpu_baseline(inp, scale, seconds_target=15.0):
+    """The fp64 oracle (naive expand-then-attend) on a bounded sample of (b, h)
+    pairs of the same workload, scaled to the step's metric."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    import oracle
+
+    w = inp["workload"]
+    T = int(inp["seqlens"][0])
+    rng = np.random.default_rng(0)
+    per_pair_flops = T * w.s_q * (2 * 576 + 2 * 512) + 2 * 2 * 128 * 512 * w.s_q
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds_target:
+        pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
+        oracle.naive_decode(inp, scale, pairs=pairs)
+        done += len(pairs)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": done * per_pair_flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} (sequence, head) pairs of the B=64 H=128 T=4096 workload, fp64 numpy naive "
+                  f"expand-then-attend, {dt:.1f} s; value = absorbed-path FLOPs of those pairs per second",
+        "tokens_per_s": done / w.H / dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; data-parallel attention would shard whole sequences per GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from head_latent_attention_mla_amd import workloads as W
+    from head_latent_attention_mla_amd import mla
+
+    w = W.WORKLOADS[args.workload]
+    scale = 1.0 / math.sqrt(192.0)
+    print(f"[bench] generating {w}", file=sys.stderr, flush=True)
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, w_uk, w_uv, cache0 = W.to_torch(inp, dev)
+    caches = [cache0]
+    for _ in range(N_COPIES - 1):
+        caches.append(mla.LatentCache(rows=cache0.rows.clone(), seqlens=cache0.seqlens, max_seqlen=cache0.max_seqlen,
+                                      row_scale=None if cache0.row_scale is None else cache0.row_scale.clone(),
+                                      block_table=cache0.block_table))
+    B, s_q, H = w.B, w.s_q, w.H
+    N = B * s_q
+    q_lat = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.empty((B, s_q, H, 512), dtype=torch.float32, device=dev)
+    out = torch.empty((B, s_q, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.decode_workspace_bytes(B, s_q, H, cache0.max_seqlen), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = caches[i % N_COPIES]
+        if ev is not None:
+            ev[0].record(stream)
+        mla.absorb_q(q.view(N, H, -1), w_uk, out=q_lat.view(N, H, -1))
+        if ev is not None:
+            ev[1].record(stream)
+        mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.decode_combine(ws, B, s_q, H, c.max_seqlen, o_lat=o_lat)
+        if ev is not None:
+            ev[3].record(stream)
+        mla.absorb_out(o_lat.view(N, H, -1), w_uv, out=out.view(N, H, -1))
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel durations with HIP events on the launch stream
+    names = ["absorb_q", "decode_split", "decode_combine", "absorb_out"]
+    tot = [0.0] * 4
+    for i in range(args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        step(i, ev)
+        torch.cuda.synchronize()
+        for k in range(4):
+            tot[k] += ev[k].elapsed_time(ev[k + 1])
+    kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
+
+    fp8 = w.cache_dtype == "fp8"
+    cnt = algorithmic_counts(B, s_q, H, [int(x) for x in inp["seqlens"]], w.causal,
+                             cache_elem_bytes=1 if fp8 else 2, scale_bytes=4 if fp8 else 0)
+    s = ms_per_step * 1e-3
+    tflops = cnt["flops_step"] / s / 1e12
+    split_s = kern_us["decode_split"] * 1e-6
+    scan_gbs = cnt["bytes_scan"] / split_s / 1e9
+    scan_tflops = cnt["flops_scan"] / split_s / 1e12
+    # the path at s_q = 1 with a bf16 cache sits below the bf16 ridge (HBM-bound);
+    # more query tokens per cached row or an fp8 cache push it past (MFMA-bound)
+    hbm_bound = (not fp8) and s_q == 1
+    roofline = {
+        "kernel": "decode_split (split-T latent scan)",
+        "bound": "hbm" if hbm_bound else "mfma",
+        "achieved": round(scan_gbs if hbm_bound else scan_tflops, 1),
+        "peak": HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS,
+        "unit": "GB/s" if hbm_bound else "TFLOP/s",
+        "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / BF16_PEAK_TFLOPS), 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": cnt["bytes_scan"],
+        "algorithmic_flops_per_launch": cnt["flops_scan"],
+        "avg_launch_us": round(kern_us["decode_split"], 2),
+        "achieved_tflops": round(scan_tflops, 1),
+        "achieved_gbs": round(scan_gbs, 1),
+    }
+    rec = {
+        "metric": "absorbed MLA decode TFLOP/s + HBM GB/s (% roofline), H=128 B=64 T=4096",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={B} H={H} s_q={s_q} T={w.T or w.T_range} "
+                               f"{'paged' if w.paged else 'contiguous'} {w.cache_dtype} latent cache [*, 576], "
+                               f"{'causal' if w.causal else 'non-causal'}, seed {w.seed}",
+                   "global_batch": B, "seq_len": w.max_T, "parallelism": "single GPU"},
+        "step_gbs": round(cnt["bytes_step"] / s / 1e9, 1),
+        "tokens_per_s": round(N / s, 1),
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(inp, scale, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

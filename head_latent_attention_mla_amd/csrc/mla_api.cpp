@@ -1,0 +1,218 @@
+// C ABI of libmla (declared in include/mla.h): argument validation, split
+// planning and kernel launches on the caller's stream.  Every check that the
+// host can make happens before the first HIP call, so a rejected call enqueues
+// nothing.
+#include "../../include/mla.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kRowsPerGroup = 128;   // query rows per decode work-group
+constexpr int kTileRows = 64;        // cached rows per LDS tile
+constexpr int kTargetWorkGroups = 256;  // one work-group per compute unit of an MI355X
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int32_t R, n_groups, n_split, split_rows, n_work, work_per_xcd;
+  size_t part_o_bytes, part_lse_bytes, ws_bytes;
+};
+
+// The split plan depends on host integers only, so the workspace size and the
+// reduction order are fixed for a given argument set.
+bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t forced, Plan* pl) {
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || forced < 0) return false;
+  const int64_t R = (int64_t)s_q * H;
+  if (R > (1 << 24) || B > (1 << 20) || max_seqlen > (1 << 28)) return false;
+  pl->R = (int32_t)R;
+  pl->n_groups = (int32_t)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int64_t tiles = (max_seqlen + kTileRows - 1) / kTileRows;
+  const int64_t base = (int64_t)B * pl->n_groups;
+  int64_t ns = forced > 0 ? forced : (kTargetWorkGroups + base - 1) / base;
+  if (ns < 1) ns = 1;
+  if (ns > tiles) ns = tiles;
+  const int64_t split_tiles = (tiles + ns - 1) / ns;
+  ns = (tiles + split_tiles - 1) / split_tiles;
+  pl->n_split = (int32_t)ns;
+  pl->split_rows = (int32_t)(split_tiles * kTileRows);
+  const int64_t n_work = base * ns;
+  if (n_work > (int64_t)1 << 30) return false;
+  pl->n_work = (int32_t)n_work;
+  pl->work_per_xcd = (int32_t)((n_work + 7) / 8);
+  pl->part_o_bytes = align_up((size_t)B * R * ns * mla::D_C * sizeof(float));
+  pl->part_lse_bytes = align_up((size_t)B * R * ns * sizeof(float));
+  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes;
+  return true;
+}
+
+mla_status check_kv(const mla_kv_desc* kv, int32_t s_q) {
+  if (kv == nullptr || kv->rows == nullptr || kv->seqlens == nullptr) return MLA_ERR_ARG;
+  if (kv->dtype != MLA_BF16 && kv->dtype != MLA_FP8_E4M3) return MLA_ERR_ARG;
+  if ((kv->dtype == MLA_FP8_E4M3) != (kv->row_scale != nullptr)) return MLA_ERR_ARG;
+  if (kv->max_seqlen <= 0 || s_q > kv->max_seqlen) return MLA_ERR_ARG;
+  if (kv->block_table != nullptr) {
+    if (kv->block_size != kTileRows) return MLA_ERR_UNSUPPORTED;
+    if (kv->max_blocks <= 0) return MLA_ERR_ARG;
+    if ((int64_t)kv->max_seqlen > (int64_t)kv->max_blocks * kTileRows) return MLA_ERR_ARG;
+  } else {
+    if (kv->T_stride <= 0) return MLA_ERR_ARG;
+    if (kv->max_seqlen > kv->T_stride) return MLA_ERR_ARG;
+  }
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_ARG: return "MLA_ERR_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: unsupported width, block size or dtype";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown mla_status";
+}
+
+mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_lat, int32_t N, int32_t H,
+                        int32_t d_nope, int32_t d_rope, int32_t d_c, void* stream) {
+  if (q == nullptr || w_uk == nullptr || q_lat == nullptr) return MLA_ERR_ARG;
+  if (N <= 0 || H <= 0 || (int64_t)N * H > (1 << 26)) return MLA_ERR_ARG;
+  if (d_nope != mla::D_NOPE || d_rope != mla::D_ROPE || d_c != mla::D_C) return MLA_ERR_UNSUPPORTED;
+  return hip_status(mla::launch_absorb_q((const uint16_t*)q, (const uint16_t*)w_uk, (uint16_t*)q_lat,
+                                         N, H, (hipStream_t)stream));
+}
+
+size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                                  int32_t num_splits) {
+  Plan pl;
+  if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return 0;
+  return pl.ws_bytes;
+}
+
+int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                              int32_t num_splits) {
+  Plan pl;
+  if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return 0;
+  return pl.n_split;
+}
+
+namespace {
+
+mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                               int32_t H, float softmax_scale, int32_t causal, void* workspace,
+                               size_t ws_bytes, int32_t num_splits, hipStream_t st) {
+  if (q_lat == nullptr) return MLA_ERR_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || num_splits < 0) return MLA_ERR_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  if (kv->dtype == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  Plan pl;
+  if (!make_plan(B, s_q, H, kv->max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
+
+  mla::DecodeParams p{};
+  p.q_lat = (const uint16_t*)q_lat;
+  p.rows = kv->rows;
+  p.row_scale = kv->row_scale;
+  p.block_table = kv->block_table;
+  p.seqlens = kv->seqlens;
+  p.part_o = (float*)workspace;
+  p.part_lse = (float*)((char*)workspace + pl.part_o_bytes);
+  p.T_stride = kv->T_stride;
+  p.max_blocks = kv->max_blocks;
+  p.B = B;
+  p.s_q = s_q;
+  p.H = H;
+  p.R = pl.R;
+  p.n_groups = pl.n_groups;
+  p.n_split = pl.n_split;
+  p.split_rows = pl.split_rows;
+  p.n_work = pl.n_work;
+  p.work_per_xcd = pl.work_per_xcd;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.causal = causal;
+  p.paged = kv->block_table != nullptr;
+  p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  return hip_status(mla::launch_decode_split(p, st));
+}
+
+mla_status decode_combine_impl(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                               int32_t num_splits, const void* workspace, size_t ws_bytes,
+                               void* o_lat, int32_t o_lat_dtype, float* lse, hipStream_t st) {
+  if (o_lat == nullptr) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  Plan pl;
+  if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
+  const float* part_o = (const float*)workspace;
+  const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
+  return hip_status(mla::launch_combine(part_o, part_lse, B, pl.R, pl.n_split, o_lat,
+                                        o_lat_dtype == MLA_BF16, lse, st));
+}
+
+}  // namespace
+
+mla_status mla_decode_partial(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                              int32_t H, float softmax_scale, int32_t causal, void* workspace,
+                              size_t ws_bytes, int32_t num_splits, void* stream) {
+  return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace, ws_bytes,
+                             num_splits, (hipStream_t)stream);
+}
+
+mla_status mla_decode_combine(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                              int32_t num_splits, const void* workspace, size_t ws_bytes,
+                              void* o_lat, int32_t o_lat_dtype, float* lse, void* stream) {
+  return decode_combine_impl(B, s_q, H, max_seqlen, num_splits, workspace, ws_bytes, o_lat,
+                             o_lat_dtype, lse, (hipStream_t)stream);
+}
+
+mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                           int32_t H, float softmax_scale, int32_t causal, void* o_lat,
+                           int32_t o_lat_dtype, float* lse, void* workspace, size_t ws_bytes,
+                           int32_t num_splits, void* stream) {
+  // validate the outputs too before anything is enqueued
+  if (o_lat == nullptr) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  const mla_status s = decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace,
+                                           ws_bytes, num_splits, (hipStream_t)stream);
+  if (s != MLA_OK) return s;
+  return decode_combine_impl(B, s_q, H, kv->max_seqlen, num_splits, workspace, ws_bytes, o_lat,
+                             o_lat_dtype, lse, (hipStream_t)stream);
+}
+
+mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_uv, void* out,
+                          int32_t N, int32_t H, int32_t d_c, int32_t d_v, void* stream) {
+  if (o_lat == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
+  if (N <= 0 || H <= 0 || (int64_t)N * H > (1 << 26)) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  if (d_c != mla::D_C || d_v != mla::D_V) return MLA_ERR_UNSUPPORTED;
+  return hip_status(mla::launch_absorb_out(o_lat, o_lat_dtype == MLA_BF16, (const uint16_t*)w_uv,
+                                           (uint16_t*)out, N, H, (hipStream_t)stream));
+}
+
+size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
+  (void)B; (void)s_q; (void)H; (void)max_seqlen;
+  return 0;
+}
+
+mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
+                            int32_t B, int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
+                            void* out, void* workspace, size_t ws_bytes, void* stream) {
+  (void)q; (void)kv; (void)w_uk; (void)w_uv; (void)B; (void)s_q; (void)H; (void)softmax_scale;
+  (void)causal; (void)out; (void)workspace; (void)ws_bytes; (void)stream;
+  return MLA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

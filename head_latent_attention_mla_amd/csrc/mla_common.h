@@ -1,0 +1,69 @@
+// Device-side helpers shared by the libmla kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// XOR pattern applied to the 16-byte chunk index of LDS row t.  For any 8
+// consecutive rows starting at a multiple of 8 it is a permutation of 0..7
+// (MFMA fragment reads: 8 lanes x 16 B on 8 rows hit distinct banks), and for
+// 4 consecutive rows starting at a multiple of 4 the chunk pairs {c, c^1}
+// (c even) map to 8 distinct chunks (transpose reads: 4 rows x 32 B).
+__device__ __forceinline__ int chunk_swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+
+// gfx950 transpose read: within each group of 16 lanes, lane j reads 4
+// consecutive 16-bit elements at its own address; lane i of the group then
+// holds element (i % 4) of lanes 4e + i/4, e = 0..3.  Used so that a lane
+// whose address points at row (base + j/4), column (cb + 4 (j%4)) receives
+// the four rows base..base+3 of column cb + i.
+__device__ __forceinline__ i16x4 ds_read_tr16(const char* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 lo, i16x4 hi) {
+  i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// MFMA with the accumulator pinned to VGPRs (for accumulators that the VALU
+// reads right after).  The hazard recognizer does not see inside inline asm:
+// after the last of these, call mfma_v_drain() on the accumulators before any
+// other instruction reads them (an MFMA result needs 12 wait states before a
+// VALU read on gfx950; the drain gives 16).  Back-to-back MFMAs accumulating
+// into the same registers need no wait states.
+__device__ __forceinline__ void mfma32_v0(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_v(f32x16& c, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v_drain(f32x16& c0, f32x16& c1) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// round-to-nearest-even float -> bf16 (hardware conversion on gfx950)
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+
+}  // namespace mla

@@ -1,0 +1,48 @@
+// Host-side launch interface between the C ABI layer (mla_api.cpp) and the
+// HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Fixed widths of the DeepSeek-V3-style latent attention.
+constexpr int D_NOPE = 128;          // per-head no-rope query/key width
+constexpr int D_ROPE = 64;           // decoupled rope key width (shared by heads)
+constexpr int D_QK = D_NOPE + D_ROPE;  // 192: query row
+constexpr int D_C = 512;             // latent width
+constexpr int D_V = 128;             // per-head value width
+constexpr int ROWW = D_C + D_ROPE;   // 576: cached row / latent query row
+
+
+// One launch of the split-T latent-attention kernel.
+struct DecodeParams {
+  const uint16_t* q_lat;        // bf16 [B, R, 576], R = s_q * H
+  const void* rows;             // cache rows (contiguous or pool), bf16 or e4m3
+  const float* row_scale;       // e4m3 only
+  const int32_t* block_table;   // paged only
+  const int32_t* seqlens;       // [B]
+  float* part_o;                // fp32 [B, n_split, 512, R], normalised partial outputs
+  float* part_lse;              // fp32 [B, n_split, R], log2-domain log-sum-exp
+  int64_t T_stride;
+  int32_t max_blocks;
+  int32_t B, s_q, H, R;
+  int32_t n_groups;             // ceil(R / 128) row groups per sequence
+  int32_t n_split, split_rows;  // split_rows is a multiple of 64
+  int32_t n_work, work_per_xcd; // B * n_split * n_groups work items over 8 XCDs
+  float scale_log2;             // softmax scale * log2(e)
+  int32_t causal;
+  int32_t paged;
+  int32_t fp8;
+};
+
+hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int R, int n_split,
+                          void* o_lat, int o_bf16, float* lse, hipStream_t stream);
+hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_lat, int N, int H,
+                           hipStream_t stream);
+hipError_t launch_absorb_out(const void* o_lat, int o_bf16, const uint16_t* w_uv, uint16_t* out,
+                             int N, int H, hipStream_t stream);
+
+}  // namespace mla

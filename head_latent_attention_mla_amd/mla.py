@@ -1,0 +1,292 @@
+"""ctypes binding of libmla (include/mla.h): argument marshalling only.
+
+Every step of the path runs in the HIP kernels of ``libmla.so``; this module
+checks tensor shapes, dtypes and devices, allocates outputs and workspaces with
+PyTorch (device memory and streams are all PyTorch is used for) and passes raw
+pointers and the current stream to the C ABI.  There is no CPU fallback: if the
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+D_NOPE, D_ROPE, D_C, D_V = 128, 64, 512, 128
+ROW = D_C + D_ROPE
+BLOCK = 64
+DEFAULT_SCALE = 1.0 / math.sqrt(D_NOPE + D_ROPE)
+
+MLA_BF16, MLA_FP8_E4M3, MLA_FP32 = 0, 1, 2
+_STATUS = {0: "MLA_OK", 1: "MLA_ERR_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE", 4: "MLA_ERR_HIP"}
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_lib.mla_status_string(status).decode()}")
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_void_p),
+        ("row_scale", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("seqlens", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("T_stride", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+    ]
+
+
+# name -> (restype, argtypes); mirrors include/mla.h
+_VP, _I32, _SZ, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "mla_absorb_q": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
+    "mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "mla_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
+    "mla_decode_attn": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _I32,
+                               _VP, _VP, _SZ, _I32, _VP]),
+    "mla_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ, _I32,
+                                  _VP]),
+    "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
+    "mla_absorb_out": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
+    "mla_naive_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_naive_decode": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP,
+                                _VP, _SZ, _VP]),
+    "mla_status_string": (ctypes.c_char_p, [_I32]),
+}
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libmla.so not built at {path}; run `python -m head_latent_attention_mla_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = load_library()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MLAError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclasses.dataclass
+class LatentCache:
+    """Device latent cache: contiguous [B, T_stride, 576] or a paged pool
+    [n_blocks, 64, 576] with an int32 block table [B, max_blocks]; bf16 rows,
+    or uint8 E4M3 codes with an fp32 per-row scale."""
+    rows: torch.Tensor
+    seqlens: torch.Tensor
+    max_seqlen: int
+    row_scale: Optional[torch.Tensor] = None
+    block_table: Optional[torch.Tensor] = None
+
+    @property
+    def fp8(self) -> bool:
+        return self.row_scale is not None
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    @property
+    def B(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    def desc(self) -> KVDesc:
+        _require(self.seqlens, "seqlens", torch.int32)
+        if self.fp8:
+            _require(self.rows, "rows", torch.uint8)
+            _require(self.row_scale, "row_scale", torch.float32, self.rows.shape[:2])
+        else:
+            _require(self.rows, "rows", torch.bfloat16)
+        if self.rows.dim() != 3 or self.rows.shape[2] != ROW:
+            raise ValueError(f"rows must be [*, *, {ROW}]")
+        d = KVDesc()
+        d.rows = self.rows.data_ptr()
+        d.row_scale = self.row_scale.data_ptr() if self.fp8 else None
+        d.seqlens = self.seqlens.data_ptr()
+        d.dtype = MLA_FP8_E4M3 if self.fp8 else MLA_BF16
+        d.max_seqlen = int(self.max_seqlen)
+        if self.paged:
+            _require(self.block_table, "block_table", torch.int32)
+            if self.block_table.shape[0] != self.B:
+                raise ValueError("block_table must have one row per sequence")
+            if self.rows.shape[1] != BLOCK:
+                raise ValueError(f"paged pool must be [n_blocks, {BLOCK}, {ROW}]")
+            d.block_table = self.block_table.data_ptr()
+            d.block_size = BLOCK
+            d.max_blocks = int(self.block_table.shape[1])
+            d.T_stride = 0
+        else:
+            if self.rows.shape[0] != self.B:
+                raise ValueError("contiguous rows must be [B, T_stride, 576]")
+            d.block_table = None
+            d.T_stride = int(self.rows.shape[1])
+            d.block_size = 0
+            d.max_blocks = 0
+        return d
+
+
+def absorb_q(q: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """q [N, H, 192] bf16, W_UK [H, 128, 512] bf16 -> latent query [N, H, 576] bf16."""
+    N, H = q.shape[0], q.shape[1]
+    _require(q, "q", torch.bfloat16, (N, H, D_NOPE + D_ROPE))
+    _require(w_uk, "w_uk", torch.bfloat16, (H, D_NOPE, D_C))
+    if out is None:
+        out = torch.empty((N, H, ROW), dtype=torch.bfloat16, device=q.device)
+    _require(out, "q_lat", torch.bfloat16, (N, H, ROW))
+    _check(_lib.mla_absorb_q(_ptr(q), _ptr(w_uk), _ptr(out), N, H, D_NOPE, D_ROPE, D_C, _stream(stream)),
+           "mla_absorb_q")
+    return out
+
+
+def decode_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0) -> int:
+    return int(_lib.mla_decode_workspace_bytes(B, s_q, H, max_seqlen, num_splits))
+
+
+def decode_num_splits(B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0) -> int:
+    return int(_lib.mla_decode_num_splits(B, s_q, H, max_seqlen, num_splits))
+
+
+def decode_attn(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_SCALE, causal: bool = False,
+                o_dtype=torch.float32, num_splits: int = 0, o_lat: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Latent attention: q_lat [B, s_q, H, 576] bf16 against the shared cache.
+    Returns (o_lat [B, s_q, H, 512] in o_dtype, lse [B, s_q, H] fp32 or None)."""
+    B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
+    if cache.B != B:
+        raise ValueError("cache holds a different number of sequences")
+    kv = cache.desc()
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=q_lat.device)
+    _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
+    if lse is None and want_lse:
+        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, s_q, H))
+    need = decode_workspace_bytes(B, s_q, H, cache.max_seqlen, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    _check(_lib.mla_decode_attn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
+                                _ptr(o_lat), dt, _ptr(lse), _ptr(workspace), workspace.numel(), num_splits,
+                                _stream(stream)), "mla_decode_attn")
+    return o_lat, lse
+
+
+def decode_partial(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_SCALE, causal: bool = False,
+                   num_splits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Phase 1 of decode_attn: the split-T scan into a workspace (returned)."""
+    B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
+    kv = cache.desc()
+    need = decode_workspace_bytes(B, s_q, H, cache.max_seqlen, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    _check(_lib.mla_decode_partial(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
+                                   _ptr(workspace), workspace.numel(), num_splits, _stream(stream)),
+           "mla_decode_partial")
+    return workspace
+
+
+def decode_combine(workspace: torch.Tensor, B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0,
+                   o_dtype=torch.float32, o_lat: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, stream=None):
+    """Phase 2 of decode_attn: merge the split partials held in ``workspace``."""
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
+    if o_lat is None:
+        o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=workspace.device)
+    _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.mla_decode_combine(B, s_q, H, max_seqlen, num_splits, _ptr(workspace), workspace.numel(),
+                                   _ptr(o_lat), dt, _ptr(lse), _stream(stream)), "mla_decode_combine")
+    return o_lat, lse
+
+
+def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """o_lat [N, H, 512] (fp32 or bf16), W_UV [H, 512, 128] bf16 -> out [N, H, 128] bf16."""
+    N, H = o_lat.shape[0], o_lat.shape[1]
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_lat.dtype]
+    _require(o_lat, "o_lat", o_lat.dtype, (N, H, D_C))
+    _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    if out is None:
+        out = torch.empty((N, H, D_V), dtype=torch.bfloat16, device=o_lat.device)
+    _require(out, "out", torch.bfloat16, (N, H, D_V))
+    _check(_lib.mla_absorb_out(_ptr(o_lat), dt, _ptr(w_uv), _ptr(out), N, H, D_C, D_V, _stream(stream)),
+           "mla_absorb_out")
+    return out
+
+
+def decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+           scale: float = DEFAULT_SCALE, causal: bool = False, o_dtype=torch.float32,
+           num_splits: int = 0, stream=None) -> torch.Tensor:
+    """Absorbed MLA decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16."""
+    B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
+    q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
+    o_lat, _ = decode_attn(q_lat, cache, scale, causal, o_dtype, num_splits, want_lse=False, stream=stream)
+    return absorb_out(o_lat.view(B * s_q, H, D_C), w_uv, stream=stream).view(B, s_q, H, D_V)
+
+
+def naive_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int) -> int:
+    return int(_lib.mla_naive_workspace_bytes(B, s_q, H, max_seqlen))
+
+
+def naive_decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                 scale: float = DEFAULT_SCALE, causal: bool = False, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Ablation: expand every cached row per head, then attend. Same I/O as decode()."""
+    B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
+    _require(q, "q", torch.bfloat16, (B, s_q, H, D_NOPE + D_ROPE))
+    _require(w_uk, "w_uk", torch.bfloat16, (H, D_NOPE, D_C))
+    _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    kv = cache.desc()
+    if out is None:
+        out = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=q.device)
+    need = naive_workspace_bytes(B, s_q, H, cache.max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.mla_naive_decode(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
+                                 int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "mla_naive_decode")
+    return out

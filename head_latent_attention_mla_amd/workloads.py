@@ -259,3 +259,29 @@ def as_contiguous(inp: dict) -> dict:
     out.update(rows=crow, row_scale=cscale, block_table=None, paged=False, T_stride=T_stride)
     out.pop("max_blocks", None)
     return out
+
+
+def to_torch(inp: dict, device="cuda"):
+    """Copy a generated input set to device tensors (bit-exact): returns
+    (q, w_uk, w_uv, cache) with cache a ``mla.LatentCache``."""
+    import torch
+    from . import mla
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+
+    q, w_uk, w_uv = bf16(inp["q"]), bf16(inp["w_uk"]), bf16(inp["w_uv"])
+    if inp["row_scale"] is not None:
+        rows = torch.from_numpy(inp["rows"]).to(device)
+        scale = torch.from_numpy(inp["row_scale"]).to(device)
+    else:
+        rows, scale = bf16(inp["rows"]), None
+    table = None if inp["block_table"] is None else torch.from_numpy(inp["block_table"]).to(device)
+    cache = mla.LatentCache(rows=rows, seqlens=torch.from_numpy(inp["seqlens"]).to(device),
+                            max_seqlen=int(inp["seqlens"].max()), row_scale=scale, block_table=table)
+    return q, w_uk, w_uv, cache
+
+
+def bf16_tensor_to_numpy_bits(t) -> np.ndarray:
+    """bf16 device tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,217 @@
+/*
+ * mla.h -- C ABI of libmla: absorbed Multi-head Latent Attention decode on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (what every entry point below is a step of):
+ *   Each query head's 128-wide no-rope part is moved into latent space through
+ *   W_UK once per query token ("absorbed" into the query), then all heads score
+ *   the same cached rows -- one 512-wide latent plus a 64-wide decoupled rope
+ *   key per token, shared by every head -- softmax the scores, average the
+ *   rows' 512 latent columns, and project that latent output back per head
+ *   through W_UV.  Sources: "MLA, dim by dim" (section "MLA Decode": decode
+ *   score order (q W_UK^T) C^T and value order (p C) W_UV, and the fused
+ *   decode kernel it sketches); "Why MLA and MTP Fight Each Other" (sections
+ *   3.1, 3.2, 4 and Appendix A); "The MLA decode speedup hiding in your model
+ *   card" ("The identity", "The absorbed form": same inputs and outputs as the
+ *   naive form, different order of multiplication).
+ *
+ * Fixed widths: d_nope = 128, d_rope = 64, d_c = 512, d_v = 128; a cached row
+ * is 576 elements [latent 0..511 | rope key 512..575]; a query row is 192
+ * elements [nope 0..127 | rope 128..191]; a latent query row is 576 elements
+ * [q_abs 0..511 | q_rope 512..575].  The rope rotation is applied by the
+ * caller before these calls (queries and cached rope keys arrive rotated).
+ *
+ * Conventions for every call:
+ *   - Every pointer is a DEVICE pointer unless marked "host".  The caller owns
+ *     all memory; the library never allocates, frees or keeps device memory.
+ *   - Tensors are dense and row-major with the last dimension contiguous.
+ *     bf16 is the 16-bit brain float; fp8 is OCP FP8 E4M3 ("e4m3fn").
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     call only enqueues work on it and returns without synchronising.
+ *   - Argument errors that the host can see are reported BEFORE any HIP call,
+ *     and then nothing has been enqueued: MLA_ERR_ARG (null pointer, size <= 0,
+ *     bad dtype, s_q > max_seqlen, ...), MLA_ERR_UNSUPPORTED (a width other than
+ *     the fixed ones above, paged block size other than 64), MLA_ERR_WORKSPACE
+ *     (workspace smaller than the *_workspace_bytes() figure).  A failed kernel
+ *     launch returns MLA_ERR_HIP.
+ *   - Device-resident values (sequence lengths, block-table entries) are not
+ *     read by the host.  Preconditions on them: s_q <= seqlens[b] <= max_seqlen,
+ *     seqlens[b] <= T_stride (contiguous) or <= max_blocks * 64 (paged), and
+ *     every block id in the first ceil(seqlens[b] / 64) entries of a row of the
+ *     block table is a valid pool block.  Entries past that are never read.
+ *   - Calls are reentrant; results for a fixed argument set are bitwise
+ *     reproducible run to run (no floating-point atomics).
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_ARG = 1,
+  MLA_ERR_UNSUPPORTED = 2,
+  MLA_ERR_WORKSPACE = 3,
+  MLA_ERR_HIP = 4
+} mla_status;
+
+typedef enum {
+  MLA_BF16 = 0,
+  MLA_FP8_E4M3 = 1,
+  MLA_FP32 = 2
+} mla_dtype;
+
+/* Description of the latent cache (a HOST struct holding device pointers).
+ *
+ * contiguous (block_table == NULL): rows is [B, T_stride, 576]; sequence b's
+ *   cached row t is rows[b, t, :].
+ * paged (block_table != NULL): rows is a pool [n_blocks, block_size, 576];
+ *   sequence b's row t is rows[block_table[b * max_blocks + t / 64], t % 64, :].
+ *   block_size must be 64.  The block layout is this library's own reading: the
+ *   pages describe only a contiguous cache.
+ * dtype MLA_BF16: rows hold bf16.  dtype MLA_FP8_E4M3: rows hold e4m3 codes and
+ *   row_scale holds one fp32 scale per row, indexed like the rows
+ *   ([B, T_stride] or [n_blocks, 64]); the cached value is code * scale (the
+ *   pages' FP8 latent cache of "Decode attention intensity...", read and
+ *   dequantised in registers).  row_scale must be NULL for bf16.
+ * seqlens: int32 [B], the number of valid rows of each sequence, including the
+ *   s_q rows of the current query tokens.
+ * max_seqlen: a host-side upper bound on every seqlens[b]; it sizes the split
+ *   plan and the workspace.
+ */
+typedef struct {
+  const void* rows;
+  const float* row_scale;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  int32_t dtype;        /* mla_dtype: MLA_BF16 or MLA_FP8_E4M3 */
+  int32_t T_stride;     /* contiguous: rows per sequence in `rows`; paged: ignored */
+  int32_t block_size;   /* paged: must be 64; contiguous: ignored */
+  int32_t max_blocks;   /* paged: columns of block_table; contiguous: ignored */
+  int32_t max_seqlen;   /* host bound on seqlens[b] */
+} mla_kv_desc;
+
+/* Step 1 -- absorb W_UK into the query ("MLA, dim by dim", "MLA Decode",
+ * decode score order; "Why MLA and MTP Fight Each Other", section 3.1).
+ *   q_lat[n, h, c]       = sum_{k<128} q[n, h, k] * w_uk[h, k, c]    (c < 512)
+ *   q_lat[n, h, 512 + r] = q[n, h, 128 + r]                          (r < 64)
+ * q      bf16 [N, H, 192]   (N = B * s_q query tokens)
+ * w_uk   bf16 [H, 128, 512] (head, d_nope, d_c)
+ * q_lat  bf16 [N, H, 576]   output; fp32 accumulation, rounded to nearest even.
+ * d_nope, d_rope, d_c must be 128, 64, 512 (else MLA_ERR_UNSUPPORTED). */
+mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_lat,
+                        int32_t N, int32_t H, int32_t d_nope, int32_t d_rope,
+                        int32_t d_c, void* stream);
+
+/* Bytes of device workspace mla_decode_attn needs for these sizes.
+ * num_splits: 0 lets the library choose the split count; a positive value
+ * forces it (any count gives the same result up to rounding).  Returns 0 for
+ * invalid sizes. */
+size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H,
+                                  int32_t max_seqlen, int32_t num_splits);
+
+/* The split count mla_decode_attn will use for these sizes (host integers only). */
+int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H,
+                              int32_t max_seqlen, int32_t num_splits);
+
+/* Steps 2 and 3 -- attention of the latent queries against the shared latent
+ * cache ("MLA, dim by dim", "MLA Decode": stream the cache blocks, online
+ * softmax, accumulate p C; "Why MLA and MTP Fight Each Other", section 4.2:
+ * each latent tile read once serves both the scores and the weighted sum).
+ * For query token j of sequence b and head h, with T = seqlens[b]:
+ *   visible rows  V = { t : t <= T - s_q + j } if causal, else { t < T }
+ *   s_t           = softmax_scale * <q_lat[b, j, h, :], row_t[0:576]>
+ *   o_lat[b,j,h,:] = sum_{t in V} softmax(s)_t * row_t[0:512]
+ *   lse[b,j,h]     = ln sum_{t in V} exp(s_t)
+ * The causal rule (the s_q newest rows are the query tokens themselves, each
+ * seeing itself and earlier rows) is this library's reading of speculative
+ * verification of s_q tokens ("Why MLA and MTP Fight Each Other", section 8).
+ * The cache is scanned in num_splits ranges of rows in parallel (split-T
+ * flash decode), each range producing a partial normalised output and its
+ * log-sum-exp in the workspace; a second kernel merges them with
+ * log-sum-exp weights.
+ * q_lat        bf16 [B, s_q, H, 576]
+ * kv           host pointer to the cache description (read during the call only)
+ * o_lat        [B, s_q, H, 512], dtype o_lat_dtype (MLA_FP32 or MLA_BF16)
+ * lse          fp32 [B, s_q, H], or NULL when not wanted
+ * workspace    device scratch of ws_bytes >= mla_decode_workspace_bytes(...);
+ *              contents on entry are ignored; it may be reused after the
+ *              stream has finished the call.
+ * num_splits   0 = library choice, else the forced split count. */
+mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
+                           int32_t B, int32_t s_q, int32_t H,
+                           float softmax_scale, int32_t causal,
+                           void* o_lat, int32_t o_lat_dtype, float* lse,
+                           void* workspace, size_t ws_bytes, int32_t num_splits,
+                           void* stream);
+
+/* Steps 2 and 3 as two separate calls, for callers that keep or move the
+ * split partials themselves (for example to merge ranges of one sequence that
+ * were scanned on different devices).  mla_decode_attn is exactly
+ * mla_decode_partial followed by mla_decode_combine on the same workspace.
+ *
+ * mla_decode_partial: same arguments as mla_decode_attn minus the outputs.
+ *   Scans split s of every sequence and writes into the workspace, with
+ *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits) and
+ *   R = s_q * H:
+ *     part_o   fp32 [B, S, 512, R] at workspace offset 0: the normalised partial
+ *              latent output of split s, column-major over the R query rows;
+ *     part_lse fp32 [B, S, R] at byte offset align256(B * S * 512 * R * 4): the
+ *              base-2 log-sum-exp of split s's scaled scores (-inf when the
+ *              split holds no visible row).
+ * mla_decode_combine: merges the S partials of every query row with weights
+ *   2^(lse_s - max_s lse_s) and writes o_lat and (if not NULL) the natural-log
+ *   lse, exactly as mla_decode_attn does.  B, s_q, H, max_seqlen and
+ *   num_splits must be those given to mla_decode_partial. */
+mla_status mla_decode_partial(const void* q_lat, const mla_kv_desc* kv,
+                              int32_t B, int32_t s_q, int32_t H,
+                              float softmax_scale, int32_t causal,
+                              void* workspace, size_t ws_bytes, int32_t num_splits,
+                              void* stream);
+mla_status mla_decode_combine(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                              int32_t num_splits, const void* workspace, size_t ws_bytes,
+                              void* o_lat, int32_t o_lat_dtype, float* lse, void* stream);
+
+/* Step 4 -- project the latent output back per head ("MLA, dim by dim",
+ * "MLA Decode", decode value order; "Why MLA and MTP Fight Each Other",
+ * section 3.2).
+ *   out[n, h, v] = sum_{c<512} o_lat[n, h, c] * w_uv[h, c, v]      (v < 128)
+ * o_lat  [N, H, 512] of dtype o_lat_dtype (MLA_FP32 or MLA_BF16).  An fp32
+ *        o_lat is split into two bf16 terms (high + low part) so that it keeps
+ *        about 16 mantissa bits through the bf16 matrix cores.
+ * w_uv   bf16 [H, 512, 128] (head, d_c, d_v)
+ * out    bf16 [N, H, 128]; fp32 accumulation, rounded to nearest even.
+ * d_c, d_v must be 512, 128 (else MLA_ERR_UNSUPPORTED). */
+mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_uv,
+                          void* out, int32_t N, int32_t H, int32_t d_c,
+                          int32_t d_v, void* stream);
+
+/* Ablation only -- the naive up-project-then-attend form ("The MLA decode
+ * speedup hiding in your model card", "The naive form, written out"; "Why MLA
+ * and MTP Fight Each Other", section 5.1, expand bracketing).  Every visible
+ * cached row is expanded per head into a 192-wide key [W_UK[h] row[0:512] |
+ * row[512:576]] and a 128-wide value row[0:512]^T W_UV[h], then ordinary
+ * softmax attention with the 192-wide query q [B, s_q, H, 192] gives
+ * out [B, s_q, H, 128] bf16.  Same inputs, outputs and causal rule as the
+ * absorbed steps 1-4 chained; about 120x their arithmetic.
+ * workspace: ws_bytes >= mla_naive_workspace_bytes(...). */
+size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
+mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv,
+                            const void* w_uk, const void* w_uv,
+                            int32_t B, int32_t s_q, int32_t H,
+                            float softmax_scale, int32_t causal, void* out,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* Static, human-readable name of a status code (host). */
+const char* mla_status_string(mla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

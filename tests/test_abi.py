@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every symbol include/mla.h declares, and
+rejects bad arguments before touching the GPU (CPU only: no call here passes
+validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+LIB = os.path.join(ROOT, "head_latent_attention_mla_amd", "libmla.so")
+
+OK, ARG, UNSUP, WS = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:mla_status|size_t|int32_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not os.path.exists(LIB):
+        pytest.skip("libmla.so not built")
+    from head_latent_attention_mla_amd import mla
+    return mla
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("mla_absorb_q", "mla_decode_attn", "mla_absorb_out", "mla_naive_decode",
+              "mla_decode_workspace_bytes", "mla_naive_workspace_bytes", "mla_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(LIB):
+        pytest.skip("libmla.so not built")
+    lib = ctypes.CDLL(LIB)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_declared_symbol(m):
+    assert set(m.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(m):
+    for s in range(5):
+        assert m._lib.mla_status_string(s).decode().startswith("MLA_")
+
+
+def test_workspace_and_split_plan(m):
+    ws = m._lib.mla_decode_workspace_bytes
+    ns = m._lib.mla_decode_num_splits
+    # DeepSeek-V3 shape: 64 sequences x 1 row group -> 4 splits of 1024 rows
+    assert ns(64, 1, 128, 4096, 0) == 4
+    assert ws(64, 1, 128, 4096, 0) == 64 * 128 * 4 * 512 * 4 + 64 * 128 * 4 * 4
+    assert ns(32, 4, 128, 8192, 0) == 2
+    assert ns(2, 1, 16, 256, 0) == 4          # capped by the number of 64-row tiles
+    assert ns(2, 1, 16, 256, 3) == 2          # 3 requested -> 2 tiles per split -> 2 splits
+    assert ns(1, 1, 128, 1, 0) == 1
+    assert ws(0, 1, 128, 100, 0) == 0 and ws(1, 1, 128, 0, 0) == 0 and ws(1, 1, 128, 10, -1) == 0
+
+
+def _kv(**kw):
+    from head_latent_attention_mla_amd.mla import KVDesc
+    d = KVDesc()
+    d.rows, d.seqlens, d.row_scale, d.block_table = 0x1000, 0x2000, None, None
+    d.dtype, d.T_stride, d.block_size, d.max_blocks, d.max_seqlen = 0, 256, 0, 0, 256
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _attn(m, kv, B=2, s_q=1, H=16, scale=0.07, causal=0, o_dtype=2, ws_bytes=1 << 30, ns=0, ql=0x3000, o=0x4000):
+    return m._lib.mla_decode_attn(ql, ctypes.byref(kv), B, s_q, H, scale, causal, o, o_dtype, None,
+                                  0x5000, ws_bytes, ns, None)
+
+
+def test_decode_attn_rejects_bad_arguments(m):
+    assert _attn(m, _kv(), ql=None) == ARG
+    assert _attn(m, _kv(), o=None) == ARG
+    assert _attn(m, _kv(rows=None)) == ARG
+    assert _attn(m, _kv(seqlens=None)) == ARG
+    assert _attn(m, _kv(), B=0) == ARG
+    assert _attn(m, _kv(), H=-1) == ARG
+    assert _attn(m, _kv(), causal=2) == ARG
+    assert _attn(m, _kv(), o_dtype=1) == ARG
+    assert _attn(m, _kv(), scale=float("nan")) == ARG
+    assert _attn(m, _kv(), ns=-1) == ARG
+    assert _attn(m, _kv(dtype=7)) == ARG
+    assert _attn(m, _kv(dtype=1)) == ARG                     # fp8 without a scale array
+    assert _attn(m, _kv(row_scale=0x6000)) == ARG            # bf16 with a scale array
+    assert _attn(m, _kv(max_seqlen=0)) == ARG
+    assert _attn(m, _kv(max_seqlen=4), s_q=5) == ARG         # s_q > max_seqlen
+    assert _attn(m, _kv(T_stride=100)) == ARG                # max_seqlen > T_stride
+    assert _attn(m, _kv(block_table=0x7000, block_size=32, max_blocks=8)) == UNSUP
+    assert _attn(m, _kv(block_table=0x7000, block_size=64, max_blocks=0)) == ARG
+    assert _attn(m, _kv(block_table=0x7000, block_size=64, max_blocks=3)) == ARG   # 3*64 < 256
+    assert _attn(m, _kv(), ws_bytes=1000) == WS
+
+
+def test_absorb_rejects_bad_arguments(m):
+    aq, ao = m._lib.mla_absorb_q, m._lib.mla_absorb_out
+    assert aq(None, 0x1, 0x2, 4, 16, 128, 64, 512, None) == ARG
+    assert aq(0x1, 0x1, 0x2, 0, 16, 128, 64, 512, None) == ARG
+    assert aq(0x1, 0x1, 0x2, 4, 16, 96, 64, 512, None) == UNSUP
+    assert aq(0x1, 0x1, 0x2, 4, 16, 128, 32, 512, None) == UNSUP
+    assert aq(0x1, 0x1, 0x2, 4, 16, 128, 64, 256, None) == UNSUP
+    assert ao(0x1, 2, None, 0x2, 4, 16, 512, 128, None) == ARG
+    assert ao(0x1, 1, 0x1, 0x2, 4, 16, 512, 128, None) == ARG    # fp8 latent output not a thing
+    assert ao(0x1, 2, 0x1, 0x2, 4, 16, 256, 128, None) == UNSUP
+    assert ao(0x1, 2, 0x1, 0x2, 4, -16, 512, 128, None) == ARG
+
+
+def test_binding_refuses_host_tensors(m):
+    import torch
+    q = torch.zeros(2, 16, 192, dtype=torch.bfloat16)
+    w = torch.zeros(16, 128, 512, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        m.absorb_q(q, w)
