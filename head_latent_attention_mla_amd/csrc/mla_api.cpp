@@ -2,7 +2,7 @@
 // planning and kernel launches on the caller's stream.  Every check that the
 // host can make happens before the first HIP call, so a rejected call enqueues
 // nothing.
-#include "../../include/mla.h"
+#include "mla.h"
 
 #include <cmath>
 #include <cstdint>
@@ -114,7 +114,7 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   if (q_lat == nullptr) return MLA_ERR_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || num_splits < 0) return MLA_ERR_ARG;
   if (causal != 0 && causal != 1) return MLA_ERR_ARG;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
   const mla_status ks = check_kv(kv, s_q);
   if (ks != MLA_OK) return ks;
   if (kv->dtype == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;

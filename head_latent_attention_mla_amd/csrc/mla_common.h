@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -12,6 +14,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
@@ -55,6 +58,46 @@ __device__ __forceinline__ void mfma32_v(f32x16& c, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void mfma_v_drain(f32x16& c0, f32x16& c1) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>{}) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
+// LDS reads issued as inline asm.  The compiler does not track these: every
+// consumer must first pass the loaded registers through wait_lgkm<N>(), which
+// waits until at most N LDS operations are outstanding (LDS operations of a
+// wave complete in order).  Used in the hot loops because the compiler's own
+// waits are conservative while direct-to-LDS loads are in flight.
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(i16x8& d, uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr16(i16x4& d, uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(addr), "i"(OFF));
+}
+template <typename R>
+__device__ __forceinline__ void touch_reg(R& r) {
+  asm volatile("" : "+v"(r));
+}
+template <int N, typename... R>
+__device__ __forceinline__ void wait_lgkm(R&... regs) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"i"(N));
+  (touch_reg(regs), ...);   // consumers depend on these, so they follow the wait
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

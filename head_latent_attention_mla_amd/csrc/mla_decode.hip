@@ -76,6 +76,29 @@ __device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
   }
 }
 
+// lanes l and l ^ 32 hold the same query row: combine their values.
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another, so swapping x with a copy of x leaves {x[l], x[l ^ 32]} in
+// the two registers of every lane.  Issued as inline asm: the compiler's own
+// builtin is treated as returning two equal values and one gets folded away.
+// The s_nop padding covers the VALU-write -> permlane-read hazard and the
+// permlane-write -> VALU-read hazard.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
 // keep a value opaque to the optimiser (stops loop-invariant hoisting of
 // per-lane address arithmetic that would otherwise pin registers)
 __device__ __forceinline__ int opaque(int x) {
@@ -87,6 +110,8 @@ template <bool PAGED>
 __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + P_BYTES];
   char* const pbuf = smem + 2 * TILE_BYTES;
+  const uint32_t smem_a = lds_addr(smem);
+  const uint32_t pbuf_a = smem_a + 2 * TILE_BYTES;
 
   // blockIdx -> work item: consecutive work items (the row groups and splits
   // of one sequence) go to the same XCD, whose L2 they share.
@@ -100,7 +125,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -128,30 +153,46 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
     }
   }
 
-  // ---- tile loader: wave w copies rows 16w..16w+15 (18 x 64 chunks of 16 B)
-  const uint16_t* rows = (const uint16_t*)p.rows;
-  auto issue_tile = [&](int tile, int buf) {
+  // ---- tile loader.  Wave w copies rows 16w..16w+15 of the tile: 18 loads
+  // of 64 lanes x 16 B, each filling 1 KB of LDS in order.  The chunk that
+  // lane l fetches for LDS slot 64 k + l follows the XOR swizzle; the pattern
+  // repeats every 8 rows (9 loads), so 9 per-lane byte offsets (< 2^14,
+  // packed two per register) cover all 18 loads.  The buffer window of a tile
+  // ends at the sequence's last row, so rows past it read as zero.
+  uint32_t loff[5] = {0, 0, 0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < 9; ++k) {
+    const int s = 64 * k + lane;
+    const int tl = s / CHUNKS;
+    const int c = (s - tl * CHUNKS) ^ chunk_swz(tl);
+    loff[k >> 1] |= (uint32_t)(tl * ROWW * 2 + c * 16) << (16 * (k & 1));
+  }
+  const char* rows = (const char*)p.rows;
+  // per-tile load state: buffer window over the tile's rows and LDS target
+  auto tile_rsrc = [&](int tile) {
     const int ts = t_begin + tile * KT;
-    const uint16_t* base;
+    const char* base;
     if (PAGED) {
       const int blk = p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)];
-      base = rows + (int64_t)blk * KT * ROWW;
+      base = rows + (int64_t)blk * KT * ROWW * 2;
     } else {
-      base = rows + ((int64_t)b * p.T_stride + ts) * ROWW;
+      base = rows + ((int64_t)b * p.T_stride + ts) * ROWW * 2;
     }
-    const int last = T - 1 - ts;   // rows past the sequence end re-read its last row
-    char* dst = smem + buf * TILE_BYTES + wave * (16 * CHUNKS * 16);
-    const int ln = opaque(lane);
-#pragma unroll
-    for (int k = 0; k < LOADS_PER_WAVE; ++k) {
-      const int s = 64 * k + ln;
-      const int tl = s / CHUNKS;                 // 0..15
-      const int pc = s - tl * CHUNKS;
-      const int c = pc ^ chunk_swz(tl);
-      const int t = min(wave * 16 + tl, last);
-      __builtin_amdgcn_global_load_lds((const void*)(base + t * ROWW + c * 8),
-                                       (lds_void_t*)(dst + k * 64 * 16), 16, 0, 0);
-    }
+    const int valid = min(KT, T - ts);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * ROWW * 2, 0x00020000);
+  };
+  const int soff = wave * (16 * ROWW * 2);
+  auto issue_load = [&](__amdgpu_buffer_rsrc_t rsrc, int buf, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int k9 = k % 9;
+    const uint32_t vo = (loff[k9 >> 1] >> (16 * (k9 & 1))) & 0xFFFFu;
+    char* dst = smem + buf * TILE_BYTES + wave * (16 * ROWW * 2) + k * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
+                                             soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+  };
+  auto issue_tile = [&](int tile, int buf) {
+    const auto rsrc = tile_rsrc(tile);
+    static_for<0, 18>([&](auto kc) { issue_load(rsrc, buf, kc); });
   };
 
   // O^T accumulators: columns 128*wave + 32*cb + ..., rows 32*rb + l32
@@ -163,11 +204,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
   float m_ref = -INFINITY;   // softmax reference of the owned row (log2 domain)
   float l_sum = 0.f;         // sum of the owned row's (rounded) probabilities
 
-  // transposed-read geometry for the value phase: lane reads row
-  // 16 kap + 4 half + rsel (+8), columns 128 wave + 32 cb + 16 grp + csel;
-  // the XOR pattern of that row is lane-constant and only the parity of cb
-  // changes the swizzled chunk, so two lane offsets cover every read
-  int pvoff[2];
+  // score-phase read geometry: row l32 (and l32 + 32), chunk 2 ks + half; the
+  // XOR pattern only touches the low 3 chunk bits, so 4 lane offsets cover all
+  // 36 k-steps (the rest is an immediate offset)
+  uint32_t qoff[4];
+  {
+    const int sw = chunk_swz(l32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qoff[i] = l32 * (CHUNKS * 16) + 16 * ((2 * i + half) ^ sw);
+  }
+  // value-phase transposed-read geometry: lane reads row 16 kap + 4 half +
+  // rsel (+8), columns 128 wave + 32 cb + 16 grp + csel; the XOR pattern of
+  // that row is lane-constant and only the parity of cb changes the swizzled
+  // chunk, so two lane offsets cover every read
+  uint32_t pvoff[2];
   {
     const int grp = (lane >> 4) & 1;
     const int rsel = (lane & 15) >> 2;
@@ -180,50 +230,71 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
       pvoff[i] = trow * (CHUNKS * 16) + 16 * (chunk ^ sw) + (csel & 7) * 2;
     }
   }
+  const uint32_t pb_lane = pbuf_a + lane * 16;
+
+  // zero both tile buffers once (LDS of rows past a sequence end stays finite)
+  for (int i = tid; i < 2 * TILE_BYTES / 16; i += NTHREADS) ((i16x8*)smem)[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  barrier_lds();
 
   if (n_tiles > 0) issue_tile(0, 0);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     barrier_tile_ready();   // tile ready; every wave is past the previous value phase
-    if (tile + 1 < n_tiles) issue_tile(tile + 1, (tile + 1) & 1);
-    const char* tb = smem + (tile & 1) * TILE_BYTES;
+    const bool has_next = tile + 1 < n_tiles;
+    const auto next = tile_rsrc(has_next ? tile + 1 : tile);
+    const int next_buf = (tile + 1) & 1;
+    const uint32_t tb_a = smem_a + (tile & 1) * TILE_BYTES;
     const int ts = t_begin + tile * KT;
 
     // ================= score phase (owned rows) =================
     bf16x8 pk[2][2];
     if (wave_on) {
       f32x16 s0, s1;
-      // row l32 (and l32 + 32), chunk 2 ks + half: the XOR pattern only
-      // touches the low 3 chunk bits, so 4 lane offsets cover all 36 k-steps
-      const int sw = chunk_swz(l32);
-      int qoff[4];
+      uint32_t qa[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qoff[i] = l32 * (CHUNKS * 16) + 16 * ((2 * i + half) ^ sw);
-#pragma unroll
-      for (int ks = 0; ks < ROWW / 16; ++ks) {
-        const char* pa = tb + qoff[ks & 3] + 128 * (ks >> 2);
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, *(const i16x8*)(pa));
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, *(const i16x8*)(pa + 32 * CHUNKS * 16));
-        if (ks == 0) {
+      for (int i = 0; i < 4; ++i) qa[i] = tb_a + qoff[i];
+      i16x8 ra[4][2];
+      auto issue_qk = [&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        lds_read_b128<128 * (ks >> 2)>(ra[ks & 3][0], qa[ks & 3]);
+        lds_read_b128<128 * (ks >> 2) + 32 * CHUNKS * 16>(ra[ks & 3][1], qa[ks & 3]);
+      };
+      static_for<0, 3>(issue_qk);
+      static_for<0, ROWW / 16>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr int ahead = (ROWW / 16 - 1 - ks) < 3 ? (ROWW / 16 - 1 - ks) : 3;
+        if constexpr (ks + 3 < ROWW / 16) issue_qk(std::integral_constant<int, ks + 3>{});
+        // the next tile's loads ride along, one per two k-steps
+        if constexpr (ks % 2 == 0) {
+          if (has_next) issue_load(next, next_buf, std::integral_constant<int, ks / 2>{});
+        }
+        wait_lgkm<2 * ahead>(ra[ks & 3][0], ra[ks & 3][1]);
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[ks & 3][0]);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[ks & 3][1]);
+        if constexpr (ks == 0) {
           mfma32_v0(s0, a0, qf[ks]);
           mfma32_v0(s1, a1, qf[ks]);
         } else {
           mfma32_v(s0, a0, qf[ks]);
           mfma32_v(s1, a1, qf[ks]);
         }
-      }
+      });
       mfma_v_drain(s0, s1);
-      float mx = -INFINITY;
+
+      // mask only where the tile reaches past a row's last visible row
+      if (__builtin_amdgcn_ballot_w64(ts + KT > lim) != 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
-        const float x0 = (t < lim) ? s0[r] * p.scale_log2 : -INFINITY;
-        const float x1 = (t + 32 < lim) ? s1[r] * p.scale_log2 : -INFINITY;
-        s0[r] = x0;
-        s1[r] = x1;
-        mx = fmaxf(mx, fmaxf(x0, x1));
+        for (int r = 0; r < 16; ++r) {
+          const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
+          s0[r] = (t < lim) ? s0[r] : -INFINITY;
+          s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // running maximum on raw scores (the scale is positive)
+      float mraw = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
+      const float mx = max_halves(mraw) * p.scale_log2;
       int kstep = 0;
       if (m_ref == -INFINITY) {
         m_ref = mx;   // first visible scores: accumulators are still zero
@@ -235,28 +306,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
           l_sum = 0.f;
         } else {
           m_ref += REF_STEP * kstep;
-          l_sum *= exp2f(-REF_STEP * kstep);
+          l_sum *= __builtin_amdgcn_exp2f(-REF_STEP * kstep);
         }
       }
-      const float mbase = (m_ref == -INFINITY) ? 0.f : m_ref;
+      const float nbase = (m_ref == -INFINITY) ? 0.f : -m_ref;
       float ls = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const __bf16 p0 = to_bf16(exp2f(s0[r] - mbase));
-        const __bf16 p1 = to_bf16(exp2f(s1[r] - mbase));
-        pk[0][r >> 3][r & 7] = p0;
-        pk[1][r >> 3][r & 7] = p1;
-        ls += (float)p0 + (float)p1;
+      for (int r = 0; r < 16; r += 2) {
+        const __bf16 p00 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
+        const __bf16 p01 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], p.scale_log2, nbase)));
+        const __bf16 p10 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
+        const __bf16 p11 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], p.scale_log2, nbase)));
+        pk[0][r >> 3][r & 7] = p00;
+        pk[0][r >> 3][(r & 7) + 1] = p01;
+        pk[1][r >> 3][r & 7] = p10;
+        pk[1][r >> 3][(r & 7) + 1] = p11;
+        ls += ((float)p00 + (float)p01) + ((float)p10 + (float)p11);
       }
-      ls += __shfl_xor(ls, 32);
-      l_sum += ls;
-      if (half == 0 && kstep != 0) {
-        // sign bits of the first three probabilities carry the reference step
+      l_sum += sum_halves(ls);
+      if (kstep != 0) {
+        // sign bits of the fragment's first three probabilities carry the
+        // reference step (both lane halves, so every reader lane sees it)
 #pragma unroll
         for (int e = 0; e < 3; ++e)
           if (kstep & (1 << e)) pk[0][0][e] = -pk[0][0][e];
       }
     } else {
+      if (has_next) static_for<0, 18>([&](auto kc) { issue_load(next, next_buf, kc); });
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -273,45 +349,67 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
 
     // ================= value phase (128 columns x all rows) =================
     {
-      // reference steps of rows 32 rb + l32, carried in the sign bits of the
-      // first three probabilities (kappa = 0 fragment, lanes of half 0)
-      float alpha[4];
-      bool any_step = false;
+      const uint32_t pa0 = tb_a + pvoff[0];
+      const uint32_t pa1 = tb_a + pvoff[1];
+      i16x8 bq[2][4];
+      i16x4 tr[2][4][2];
+      auto issue_pv = [&](auto kc) {
+        constexpr int kap = decltype(kc)::value;
+        constexpr int slot = kap & 1;
+        static_for<0, 4>([&](auto rbc) {
+          constexpr int rb = decltype(rbc)::value;
+          lds_read_b128<(rb * 4 + kap) * 1024>(bq[slot][rb], pb_lane);
+        });
+        static_for<0, 4>([&](auto cbc) {
+          constexpr int cb = decltype(cbc)::value;
+          constexpr int off = 16 * kap * (CHUNKS * 16) + 128 * (cb >> 1);
+          const uint32_t a = (cb & 1) ? pa1 : pa0;
+          lds_read_tr16<off>(tr[slot][cb][0], a);
+          lds_read_tr16<off + 8 * CHUNKS * 16>(tr[slot][cb][1], a);
+        });
+      };
+      issue_pv(std::integral_constant<int, 0>{});
+      static_for<0, 4>([&](auto kc) {
+        constexpr int kap = decltype(kc)::value;
+        constexpr int slot = kap & 1;
+        wait_lgkm<0>(bq[slot][0], bq[slot][1], bq[slot][2], bq[slot][3],
+                     tr[slot][0][0], tr[slot][0][1], tr[slot][1][0], tr[slot][1][1],
+                     tr[slot][2][0], tr[slot][2][1], tr[slot][3][0], tr[slot][3][1]);
+        if constexpr (kap + 1 < 4) issue_pv(std::integral_constant<int, kap + 1>{});
+        if constexpr (kap == 0) {
+          // reference steps of rows 32 rb + l32, carried in the sign bits of
+          // the first three probabilities of the kappa = 0 fragment
+          float alpha[4];
+          bool any_step = false;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const i16x8 v = *(const i16x8*)(pbuf + ((rb * 4) * 64 + lane) * 16);
-        int code = 0;
-        if (half == 0) code = ((v[0] >> 15) & 1) | (((v[1] >> 15) & 1) << 1) | (((v[2] >> 15) & 1) << 2);
-        code |= __shfl_xor(code, 32);
-        alpha[rb] = code == 0 ? 1.0f : (code == 7 ? 0.0f : exp2f(-REF_STEP * code));
-        any_step |= code != 0;
-      }
-      if (__builtin_amdgcn_ballot_w64(any_step) != 0) {
+          for (int rb = 0; rb < 4; ++rb) {
+            const uint32_t d0 = (uint32_t)__builtin_bit_cast(u32x4, bq[0][rb])[0];
+            const uint32_t d1 = (uint32_t)__builtin_bit_cast(u32x4, bq[0][rb])[1];
+            const int code = (int)(((d0 >> 15) & 1u) | ((d0 >> 30) & 2u) | ((d1 >> 13) & 4u));
+            alpha[rb] = code == 0 ? 1.0f : (code == 7 ? 0.0f : __builtin_amdgcn_exp2f(-REF_STEP * code));
+            any_step |= code != 0;
+          }
+          if (__builtin_amdgcn_ballot_w64(any_step) != 0) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+            for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int rb = 0; rb < 4; ++rb) scale_acc(acc[cb][rb], alpha[rb]);
-      }
-    }
+              for (int rb = 0; rb < 4; ++rb) scale_acc(acc[cb][rb], alpha[rb]);
+          }
+        }
+        bf16x8 bb[4];
 #pragma unroll
-    for (int kap = 0; kap < 4; ++kap) {
-      bf16x8 bq[4];
+        for (int rb = 0; rb < 4; ++rb) {
+          u32x4 v = __builtin_bit_cast(u32x4, bq[slot][rb]);
+          v &= 0x7FFF7FFFu;
+          bb[rb] = __builtin_bit_cast(bf16x8, v);
+        }
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        i16x8 v = *(const i16x8*)(pbuf + ((rb * 4 + kap) * 64 + lane) * 16);
-        v &= (short)0x7FFF;
-        bq[rb] = __builtin_bit_cast(bf16x8, v);
-      }
-      const char* prow = tb + (16 * kap) * (CHUNKS * 16);
+        for (int cb = 0; cb < 4; ++cb) {
+          const bf16x8 a = join_tr(tr[slot][cb][0], tr[slot][cb][1]);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const char* pa = prow + pvoff[cb & 1] + 128 * (cb >> 1);
-        const i16x4 lo = ds_read_tr16(pa);
-        const i16x4 hi = ds_read_tr16(pa + 8 * CHUNKS * 16);
-        const bf16x8 a = join_tr(lo, hi);
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[cb][rb] = mfma32(a, bq[rb], acc[cb][rb]);
-      }
+          for (int rb = 0; rb < 4; ++rb) acc[cb][rb] = mfma32(a, bb[rb], acc[cb][rb]);
+        }
+      });
     }
   }
 
