@@ -151,15 +151,18 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # per-kernel durations with HIP events on the launch stream
+    # per-kernel durations with HIP events on the launch stream (recorded
+    # back to back, read after one synchronisation)
     names = ["absorb_q", "decode_split", "decode_combine", "absorb_out"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     tot = [0.0] * 4
     for i in range(args.steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        step(i, ev)
-        torch.cuda.synchronize()
         for k in range(4):
-            tot[k] += ev[k].elapsed_time(ev[k + 1])
+            tot[k] += evs[i][k].elapsed_time(evs[i][k + 1])
     kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
 
     fp8 = w.cache_dtype == "fp8"

@@ -117,7 +117,6 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
   const mla_status ks = check_kv(kv, s_q);
   if (ks != MLA_OK) return ks;
-  if (kv->dtype == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
   Plan pl;
   if (!make_plan(B, s_q, H, kv->max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;

@@ -29,9 +29,8 @@
 // multiplies that row's accumulators by 2^(-64 k).
 //
 // The cache is split along T into n_split ranges; each (sequence, range, row
-// group) is one work-group writing a normalised partial output ([c][row]
-// major, so stores are row-contiguous) and its log2-domain log-sum-exp.  The
-// combine kernel merges the ranges.
+// group) is one work-group writing a normalised partial output row per query
+// row and its log2-domain log-sum-exp.  The combine kernel merges the ranges.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -88,6 +87,14 @@ __device__ __forceinline__ void halves(float x, float& a, float& b) {
   b = x;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+// max of three, without the NaN-quieting the compiler adds around fmaxf on
+// values it cannot see (scores are finite or -inf)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float max_halves(float x) {
   float a, b;
   halves(x, a, b);
@@ -106,8 +113,15 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-template <bool PAGED>
-__global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodeParams p) {
+// LDS layout.  bf16 cache: two tile buffers (double-buffered loads) + P.
+// FP8 cache: one bf16 tile buffer, two staging buffers for the e4m3 codes
+// (double-buffered loads) + P; each tile is converted codes * row scale ->
+// bf16 into the tile buffer, after which both paths are identical.
+constexpr int STAGE_BYTES = KT * ROWW;        // 36,864: e4m3 codes of one tile
+static_assert(TILE_BYTES + 2 * STAGE_BYTES == 2 * TILE_BYTES, "layouts share the P offset");
+
+template <bool PAGED, bool FP8>
+__global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + P_BYTES];
   char* const pbuf = smem + 2 * TILE_BYTES;
   const uint32_t smem_a = lds_addr(smem);
@@ -168,31 +182,65 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
     loff[k >> 1] |= (uint32_t)(tl * ROWW * 2 + c * 16) << (16 * (k & 1));
   }
   const char* rows = (const char*)p.rows;
-  // per-tile load state: buffer window over the tile's rows and LDS target
+  constexpr int ELEM = FP8 ? 1 : 2;            // bytes per cached element
+  // per-tile load state: buffer window over the tile's rows
+  auto tile_base = [&](int tile) -> int64_t {  // element index of the tile's first row
+    const int ts = t_begin + tile * KT;
+    if (PAGED) return (int64_t)p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)] * KT;
+    return (int64_t)b * p.T_stride + ts;
+  };
   auto tile_rsrc = [&](int tile) {
     const int ts = t_begin + tile * KT;
-    const char* base;
-    if (PAGED) {
-      const int blk = p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)];
-      base = rows + (int64_t)blk * KT * ROWW * 2;
-    } else {
-      base = rows + ((int64_t)b * p.T_stride + ts) * ROWW * 2;
-    }
     const int valid = min(KT, T - ts);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * ROWW * 2, 0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW * ELEM), (short)0,
+                                             valid * ROWW * ELEM, 0x00020000);
   };
-  const int soff = wave * (16 * ROWW * 2);
+  const int soff = wave * (16 * ROWW * ELEM);
   auto issue_load = [&](__amdgpu_buffer_rsrc_t rsrc, int buf, auto kc) {
     constexpr int k = decltype(kc)::value;
-    constexpr int k9 = k % 9;
-    const uint32_t vo = (loff[k9 >> 1] >> (16 * (k9 & 1))) & 0xFFFFu;
-    char* dst = smem + buf * TILE_BYTES + wave * (16 * ROWW * 2) + k * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
-                                             soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+    if constexpr (FP8) {
+      // 16 rows of codes are 9 KB contiguous: plain lane order into staging
+      char* dst = smem + TILE_BYTES + buf * STAGE_BYTES + wave * (16 * ROWW) + k * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0, 0);
+    } else {
+      constexpr int k9 = k % 9;
+      const uint32_t vo = (loff[k9 >> 1] >> (16 * (k9 & 1))) & 0xFFFFu;
+      char* dst = smem + buf * TILE_BYTES + wave * (16 * ROWW * 2) + k * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
+                                               soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+    }
   };
+  constexpr int NLOADS = FP8 ? 9 : 18;         // 1 KB loads per wave per tile
   auto issue_tile = [&](int tile, int buf) {
     const auto rsrc = tile_rsrc(tile);
-    static_for<0, 18>([&](auto kc) { issue_load(rsrc, buf, kc); });
+    static_for<0, NLOADS>([&](auto kc) { issue_load(rsrc, buf, kc); });
+  };
+  // FP8: thread tid converts row tid / 4 of a tile, quarter tid % 4 (144 codes);
+  // its row scale is fetched one tile ahead
+  const int cv_row = tid >> 2, cv_q = tid & 3;
+  auto load_scale = [&](int tile) -> float {
+    const int ts = t_begin + tile * KT;
+    return (ts + cv_row < T) ? p.row_scale[tile_base(tile) + cv_row] : 0.f;
+  };
+  auto convert_tile = [&](int buf, float scale) {
+    const char* src = smem + TILE_BYTES + buf * STAGE_BYTES + cv_row * ROWW;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int m = cv_q * 9 + i;                 // 16-code chunk of the row
+      const u32x4 w = *(const u32x4*)(src + m * 16);
+      i16x8 o[2];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
+        o[d >> 1][4 * (d & 1) + 0] = (short)bf16_bits(to_bf16(lo[0] * scale));
+        o[d >> 1][4 * (d & 1) + 1] = (short)bf16_bits(to_bf16(lo[1] * scale));
+        o[d >> 1][4 * (d & 1) + 2] = (short)bf16_bits(to_bf16(hi[0] * scale));
+        o[d >> 1][4 * (d & 1) + 3] = (short)bf16_bits(to_bf16(hi[1] * scale));
+      }
+      *(i16x8*)(smem + lds_off(cv_row, 16 * m)) = o[0];
+      *(i16x8*)(smem + lds_off(cv_row, 16 * m + 8)) = o[1];
+    }
   };
 
   // O^T accumulators: columns 128*wave + 32*cb + ..., rows 32*rb + l32
@@ -236,14 +284,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
   for (int i = tid; i < 2 * TILE_BYTES / 16; i += NTHREADS) ((i16x8*)smem)[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
   barrier_lds();
 
-  if (n_tiles > 0) issue_tile(0, 0);
+  float sc_cur = 0.f, sc_next = 0.f;            // FP8 row scales (this tile, next)
+  if (n_tiles > 0) {
+    issue_tile(0, 0);
+    if constexpr (FP8) sc_next = load_scale(0);
+  }
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     barrier_tile_ready();   // tile ready; every wave is past the previous value phase
     const bool has_next = tile + 1 < n_tiles;
     const auto next = tile_rsrc(has_next ? tile + 1 : tile);
     const int next_buf = (tile + 1) & 1;
-    const uint32_t tb_a = smem_a + (tile & 1) * TILE_BYTES;
+    uint32_t tb_a;
+    if constexpr (FP8) {
+      // dequantise the staged codes into the bf16 tile buffer; rows past the
+      // sequence end have scale 0 and become zeros
+      sc_cur = sc_next;
+      if (has_next) sc_next = load_scale(tile + 1);
+      convert_tile(tile & 1, sc_cur);
+      barrier_lds();
+      tb_a = smem_a;
+    } else {
+      tb_a = smem_a + (tile & 1) * TILE_BYTES;
+    }
     const int ts = t_begin + tile * KT;
 
     // ================= score phase (owned rows) =================
@@ -265,8 +328,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
         constexpr int ahead = (ROWW / 16 - 1 - ks) < 3 ? (ROWW / 16 - 1 - ks) : 3;
         if constexpr (ks + 3 < ROWW / 16) issue_qk(std::integral_constant<int, ks + 3>{});
         // the next tile's loads ride along, one per two k-steps
-        if constexpr (ks % 2 == 0) {
-          if (has_next) issue_load(next, next_buf, std::integral_constant<int, ks / 2>{});
+        constexpr int every = FP8 ? 4 : 2;
+        if constexpr (ks % every == 0 && ks / every < NLOADS) {
+          if (has_next) issue_load(next, next_buf, std::integral_constant<int, ks / every>{});
         }
         wait_lgkm<2 * ahead>(ra[ks & 3][0], ra[ks & 3][1]);
         const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[ks & 3][0]);
@@ -291,38 +355,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
         }
       }
       // running maximum on raw scores (the scale is positive)
-      float mraw = -INFINITY;
+      float mraw = max3f(s0[0], s0[1], s1[0]);
+      mraw = max3f(mraw, s1[1], s0[2]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
+      for (int r = 2; r < 14; r += 2) {
+        mraw = max3f(mraw, s1[r], s0[r + 1]);
+        mraw = max3f(mraw, s1[r + 1], s0[r + 2]);
+      }
+      mraw = max3f(mraw, s1[14], s0[15]);
+      mraw = fmaxf(mraw, s1[15]);
       const float mx = max_halves(mraw) * p.scale_log2;
-      int kstep = 0;
-      if (m_ref == -INFINITY) {
-        m_ref = mx;   // first visible scores: accumulators are still zero
-      } else if (mx > m_ref + REF_STEP) {
-        kstep = (int)ceilf((mx - m_ref - REF_STEP) * (1.0f / REF_STEP));
-        if (kstep >= 7) {
-          kstep = 7;          // everything so far is below 2^-448 of the new scale
-          m_ref = mx;
-          l_sum = 0.f;
-        } else {
-          m_ref += REF_STEP * kstep;
-          l_sum *= __builtin_amdgcn_exp2f(-REF_STEP * kstep);
-        }
-      }
+      // reference update, branch-free: the first visible scores set it; later
+      // it moves up in steps of REF_STEP only when the maximum passes it by more
+      const bool first = m_ref == -INFINITY;
+      const float over = (mx - m_ref - REF_STEP) * (1.0f / REF_STEP);
+      const int kraw = (!first && over > 0.f) ? (int)ceilf(over) : 0;
+      const int kstep = kraw > 7 ? 7 : kraw;
+      l_sum = kstep == 7 ? 0.f : l_sum * __builtin_amdgcn_exp2f(-REF_STEP * kstep);
+      m_ref = (first || kstep == 7) ? mx : m_ref + REF_STEP * kstep;
       const float nbase = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      float ls = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const __bf16 p00 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
-        const __bf16 p01 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], p.scale_log2, nbase)));
-        const __bf16 p10 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
-        const __bf16 p11 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], p.scale_log2, nbase)));
-        pk[0][r >> 3][r & 7] = p00;
-        pk[0][r >> 3][(r & 7) + 1] = p01;
-        pk[1][r >> 3][r & 7] = p10;
-        pk[1][r >> 3][(r & 7) + 1] = p11;
-        ls += ((float)p00 + (float)p01) + ((float)p10 + (float)p11);
+      for (int r = 0; r < 16; ++r) {
+        pk[0][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
+        pk[1][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
       }
+      // row sum of the rounded probabilities, two at a time
+      float ls = 0.f;
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pk[sb][j][e], pk[sb][j][e + 1]};
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+          }
       l_sum += sum_halves(ls);
       if (kstep != 0) {
         // sign bits of the fragment's first three probabilities carry the
@@ -332,7 +400,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
           if (kstep & (1 << e)) pk[0][0][e] = -pk[0][0][e];
       }
     } else {
-      if (has_next) static_for<0, 18>([&](auto kc) { issue_load(next, next_buf, kc); });
+      if (has_next) static_for<0, NLOADS>([&](auto kc) { issue_load(next, next_buf, kc); });
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -345,21 +413,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
       for (int j = 0; j < 2; ++j)
         *(bf16x8*)(pbuf + ((wave * 4 + 2 * sb + j) * 64 + lane) * 16) = pk[sb][j];
 
-    barrier_lds();   // probabilities of all 128 rows visible
-
     // ================= value phase (128 columns x all rows) =================
     {
       const uint32_t pa0 = tb_a + pvoff[0];
       const uint32_t pa1 = tb_a + pvoff[1];
       i16x8 bq[2][4];
       i16x4 tr[2][4][2];
-      auto issue_pv = [&](auto kc) {
+      auto issue_tr = [&](auto kc) {
         constexpr int kap = decltype(kc)::value;
         constexpr int slot = kap & 1;
-        static_for<0, 4>([&](auto rbc) {
-          constexpr int rb = decltype(rbc)::value;
-          lds_read_b128<(rb * 4 + kap) * 1024>(bq[slot][rb], pb_lane);
-        });
         static_for<0, 4>([&](auto cbc) {
           constexpr int cb = decltype(cbc)::value;
           constexpr int off = 16 * kap * (CHUNKS * 16) + 128 * (cb >> 1);
@@ -368,7 +430,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
           lds_read_tr16<off + 8 * CHUNKS * 16>(tr[slot][cb][1], a);
         });
       };
-      issue_pv(std::integral_constant<int, 0>{});
+      auto issue_bq = [&](auto kc) {
+        constexpr int kap = decltype(kc)::value;
+        constexpr int slot = kap & 1;
+        static_for<0, 4>([&](auto rbc) {
+          constexpr int rb = decltype(rbc)::value;
+          lds_read_b128<(rb * 4 + kap) * 1024>(bq[slot][rb], pb_lane);
+        });
+      };
+      auto issue_pv = [&](auto kc) {
+        issue_tr(kc);
+        issue_bq(kc);
+      };
+      // the first transposed tile reads only need the tile: issue them before
+      // the barrier that publishes the probabilities
+      issue_tr(std::integral_constant<int, 0>{});
+      barrier_lds();   // probabilities of all 128 rows visible
+      issue_bq(std::integral_constant<int, 0>{});
       static_for<0, 4>([&](auto kc) {
         constexpr int kap = decltype(kc)::value;
         constexpr int slot = kap & 1;
@@ -419,19 +497,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
   if (half == 0) lsh[wave * 32 + l32] = l_sum;
   barrier_lds();
 
-  const int64_t pbase = ((int64_t)b * p.n_split + split) * D_C;
+  // partial rows are row-major [B][n_split][R][512]: a lane pair covers 128
+  // contiguous bytes of one row per (cb, rb), stored back to back
+  const int64_t pbase = ((int64_t)b * p.n_split + split) * p.R;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int row = g * 128 + rb * 32 + l32;
     if (row >= p.R) continue;
     const float l = lsh[rb * 32 + l32];
     const float inv = l > 0.f ? 1.0f / l : 0.f;
+    float* prow = p.part_o + (pbase + row) * D_C + wave * 128 + 4 * half;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = wave * 128 + cb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        p.part_o[(pbase + c) * p.R + row] = acc[cb][rb][r] * inv;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = {acc[cb][rb][4 * q4] * inv, acc[cb][rb][4 * q4 + 1] * inv,
+                         acc[cb][rb][4 * q4 + 2] * inv, acc[cb][rb][4 * q4 + 3] * inv};
+        *(f32x4*)(prow + cb * 32 + 8 * q4) = v;
       }
     }
   }
@@ -440,70 +522,69 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_bf16_kernel(DecodePa
         l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
 }
 
-// Merge the split partials.  Work-group = 64 query rows x 64 latent columns
-// of one sequence; thread (row, 16-column slice).  Weights 2^(lse_s - max).
+// Merge the split partials of each query row: weights 2^(lse_s - max_s),
+// then the weighted mean of the normalised partial rows.  One thread per
+// (row, 4 latent columns); partial and output rows are contiguous, so every
+// load and store is coalesced.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       int B, int R, int n_split,
                                                       void* o_lat, int o_bf16, float* lse_out) {
-  const int b = blockIdx.z;
-  const int row = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int c0 = blockIdx.y * 64 + (threadIdx.x >> 6) * 16;
-  if (row >= R) return;
+  const int64_t row_g = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);   // b * R + row
+  if (row_g >= (int64_t)B * R) return;
+  const int b = (int)(row_g / R);
+  const int row = (int)(row_g - (int64_t)b * R);
+  const int c4 = (threadIdx.x & 127) * 4;
+  const int64_t sb = (int64_t)b * n_split;
   float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s)
-    mx = fmaxf(mx, part_lse[((int64_t)b * n_split + s) * R + row]);
+  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(sb + s) * R + row]);
   float wsum = 0.f;
-  float acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < n_split; ++s) {
-    const float ls = part_lse[((int64_t)b * n_split + s) * R + row];
+    const float ls = part_lse[(sb + s) * R + row];
     if (ls == -INFINITY) continue;
     const float w = exp2f(ls - mx);
     wsum += w;
-    const float* src = part_o + (((int64_t)b * n_split + s) * D_C + c0) * R + row;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += w * src[(int64_t)i * R];
+    acc += w * *(const f32x4*)(part_o + ((sb + s) * R + row) * D_C + c4);
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  const int64_t orow = (int64_t)b * R + row;
+  acc *= inv;
   if (o_bf16) {
-    uint16_t* o = (uint16_t*)o_lat + orow * D_C + c0;
-    i16x8 v0, v1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v0[i] = (short)bf16_bits(to_bf16(acc[i] * inv));
-      v1[i] = (short)bf16_bits(to_bf16(acc[i + 8] * inv));
-    }
-    *(i16x8*)o = v0;
-    *(i16x8*)(o + 8) = v1;
+    const uint64_t packed = (uint64_t)bf16_bits(to_bf16(acc[0])) |
+                            ((uint64_t)bf16_bits(to_bf16(acc[1])) << 16) |
+                            ((uint64_t)bf16_bits(to_bf16(acc[2])) << 32) |
+                            ((uint64_t)bf16_bits(to_bf16(acc[3])) << 48);
+    *(uint64_t*)((uint16_t*)o_lat + row_g * D_C + c4) = packed;
   } else {
-    float* o = (float*)o_lat + orow * D_C + c0;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4)
-      *(f32x4*)(o + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
+    *(f32x4*)((float*)o_lat + row_g * D_C + c4) = acc;
   }
-  if (lse_out != nullptr && blockIdx.y == 0 && threadIdx.x < 64)
-    lse_out[orow] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
+  if (lse_out != nullptr && (threadIdx.x & 127) == 0)
+    lse_out[row_g] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream) {
   const int grid = 8 * p.work_per_xcd;
-  if (p.paged)
-    hipLaunchKernelGGL(decode_split_bf16_kernel<true>, dim3(grid), dim3(NTHREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL(decode_split_bf16_kernel<false>, dim3(grid), dim3(NTHREADS), 0, stream, p);
+  if (p.paged) {
+    if (p.fp8)
+      hipLaunchKernelGGL((decode_split_kernel<true, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<true, false>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  } else {
+    if (p.fp8)
+      hipLaunchKernelGGL((decode_split_kernel<false, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<false, false>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int R, int n_split,
                           void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
-  dim3 grid((R + 63) / 64, D_C / 64, B);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, stream, part_o, part_lse, B, R, n_split,
-                     o_lat, o_bf16, lse);
+  const int64_t rows = (int64_t)B * R;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, part_o, part_lse,
+                     B, R, n_split, o_lat, o_bf16, lse);
   return hipGetLastError();
 }
 

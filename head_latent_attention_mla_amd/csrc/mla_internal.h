@@ -23,7 +23,7 @@ struct DecodeParams {
   const float* row_scale;       // e4m3 only
   const int32_t* block_table;   // paged only
   const int32_t* seqlens;       // [B]
-  float* part_o;                // fp32 [B, n_split, 512, R], normalised partial outputs
+  float* part_o;                // fp32 [B, n_split, R, 512], normalised partial outputs
   float* part_lse;              // fp32 [B, n_split, R], log2-domain log-sum-exp
   int64_t T_stride;
   int32_t max_blocks;

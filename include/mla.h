@@ -159,8 +159,8 @@ mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
  *   Scans split s of every sequence and writes into the workspace, with
  *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits) and
  *   R = s_q * H:
- *     part_o   fp32 [B, S, 512, R] at workspace offset 0: the normalised partial
- *              latent output of split s, column-major over the R query rows;
+ *     part_o   fp32 [B, S, R, 512] at workspace offset 0: the normalised partial
+ *              latent output of split s for each of the R query rows;
  *     part_lse fp32 [B, S, R] at byte offset align256(B * S * 512 * R * 4): the
  *              base-2 log-sum-exp of split s's scaled scores (-inf when the
  *              split holds no visible row).
