@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--naive-steps", type=int, default=3,
+                    help="calls of the naive expand-then-attend ablation to time (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
@@ -212,6 +214,27 @@ def main():
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
     }
+    if args.naive_steps > 0:
+        # the ablation: same inputs and output, every cached row expanded per head
+        nws = torch.empty(mla.naive_workspace_bytes(B, s_q, H, cache0.max_seqlen), dtype=torch.uint8, device=dev)
+        out_n = torch.empty_like(out)
+        mla.naive_decode(q, cache0, w_uk, w_uv, scale, w.causal, out=out_n, workspace=nws)
+        torch.cuda.synchronize()
+        n0, n1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n0.record(stream)
+        for i in range(args.naive_steps):
+            mla.naive_decode(q, caches[i % N_COPIES], w_uk, w_uv, scale, w.causal, out=out_n, workspace=nws)
+        n1.record(stream)
+        torch.cuda.synchronize()
+        naive_ms = n0.elapsed_time(n1) / args.naive_steps
+        naive_flops = cnt["flops_scan"] // (2 * 576 + 2 * 512) * (2 * 192 + 2 * 128) + \
+            sum(int(x) for x in inp["seqlens"]) * H * 2 * (2 * 512 * 128)
+        rec["naive_ablation"] = {
+            "ms_per_step": round(naive_ms, 4),
+            "absorbed_speedup": round(naive_ms / ms_per_step, 2),
+            "naive_algorithmic_tflops": round(naive_flops / (naive_ms * 1e-3) / 1e12, 1),
+            "naive_flops": naive_flops,
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(inp, scale, args.cpu_seconds)

@@ -202,16 +202,42 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
 }
 
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
-  (void)B; (void)s_q; (void)H; (void)max_seqlen;
-  return 0;
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || H > (1 << 16)) return 0;
+  // W_UV re-laid out per head with the latent dimension contiguous
+  return align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t));
 }
 
 mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
                             int32_t B, int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
                             void* out, void* workspace, size_t ws_bytes, void* stream) {
-  (void)q; (void)kv; (void)w_uk; (void)w_uv; (void)B; (void)s_q; (void)H; (void)softmax_scale;
-  (void)causal; (void)out; (void)workspace; (void)ws_bytes; (void)stream;
-  return MLA_ERR_UNSUPPORTED;
+  if (q == nullptr || w_uk == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || H > (1 << 16) || B > (1 << 16)) return MLA_ERR_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  if (s_q > mla::NAIVE_MAX_SQ) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla_naive_workspace_bytes(B, s_q, H, kv->max_seqlen);
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  mla::NaiveParams p{};
+  p.q = (const uint16_t*)q;
+  p.rows = kv->rows;
+  p.row_scale = kv->row_scale;
+  p.block_table = kv->block_table;
+  p.seqlens = kv->seqlens;
+  p.w_uk = (const uint16_t*)w_uk;
+  p.w_uv = (const uint16_t*)w_uv;
+  p.w_uvt = (uint16_t*)workspace;
+  p.out = (uint16_t*)out;
+  p.T_stride = kv->T_stride;
+  p.max_blocks = kv->max_blocks;
+  p.B = B;
+  p.s_q = s_q;
+  p.H = H;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.causal = causal;
+  p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  return hip_status(mla::launch_naive(p, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -37,6 +37,26 @@ struct DecodeParams {
   int32_t fp8;
 };
 
+// One call of the naive (expand-then-attend) ablation.
+struct NaiveParams {
+  const uint16_t* q;            // bf16 [B, s_q, H, 192]
+  const void* rows;             // cache rows (contiguous or pool), bf16 or e4m3
+  const float* row_scale;       // e4m3 only
+  const int32_t* block_table;   // paged only (else null)
+  const int32_t* seqlens;       // [B]
+  const uint16_t* w_uk;         // bf16 [H, 128, 512]
+  const uint16_t* w_uv;         // bf16 [H, 512, 128]
+  uint16_t* w_uvt;              // workspace: bf16 [H, 128, 512]
+  uint16_t* out;                // bf16 [B, s_q, H, 128]
+  int64_t T_stride;
+  int32_t max_blocks;
+  int32_t B, s_q, H;
+  float scale_log2;
+  int32_t causal;
+  int32_t fp8;
+};
+constexpr int NAIVE_MAX_SQ = 4;
+
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int R, int n_split,
                           void* o_lat, int o_bf16, float* lse, hipStream_t stream);
@@ -44,5 +64,6 @@ hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_
                            hipStream_t stream);
 hipError_t launch_absorb_out(const void* o_lat, int o_bf16, const uint16_t* w_uv, uint16_t* out,
                              int N, int H, hipStream_t stream);
+hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -199,7 +199,12 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
  * softmax attention with the 192-wide query q [B, s_q, H, 192] gives
  * out [B, s_q, H, 128] bf16.  Same inputs, outputs and causal rule as the
  * absorbed steps 1-4 chained; about 120x their arithmetic.
- * workspace: ws_bytes >= mla_naive_workspace_bytes(...). */
+ * Expanded keys and values are rounded to bf16 (as a materialised bf16 K/V
+ * would be); scores, softmax and the value sum accumulate in fp32.
+ * s_q must be <= 4 (else MLA_ERR_UNSUPPORTED).  softmax_scale finite and > 0.
+ * workspace: ws_bytes >= mla_naive_workspace_bytes(...) (= H * 128 * 512 * 2
+ * rounded up to 256, a per-head transposed copy of W_UV written by the call);
+ * 0 from mla_naive_workspace_bytes means an invalid size argument. */
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
 mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv,
                             const void* w_uk, const void* w_uv,

@@ -121,3 +121,22 @@ def test_binding_refuses_host_tensors(m):
     w = torch.zeros(16, 128, 512, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         m.absorb_q(q, w)
+
+
+def _naive(m, kv, B=2, s_q=1, H=16, scale=0.07, causal=0, ws_bytes=1 << 30, q=0x3000, out=0x4000):
+    return m._lib.mla_naive_decode(q, ctypes.byref(kv), 0x6000, 0x7000, B, s_q, H, scale, causal, out,
+                                   0x5000, ws_bytes, None)
+
+
+def test_naive_rejects_bad_arguments(m):
+    ws = m._lib.mla_naive_workspace_bytes
+    assert ws(2, 1, 16, 256) == 16 * 128 * 512 * 2
+    assert ws(0, 1, 16, 256) == 0 and ws(2, 1, 16, 0) == 0
+    assert _naive(m, _kv(), q=None) == ARG
+    assert _naive(m, _kv(), out=None) == ARG
+    assert _naive(m, _kv(rows=None)) == ARG
+    assert _naive(m, _kv(), causal=3) == ARG
+    assert _naive(m, _kv(), scale=-1.0) == ARG
+    assert _naive(m, _kv(max_seqlen=8), s_q=5) == UNSUP     # at most 4 query tokens
+    assert _naive(m, _kv(block_table=0x7000, block_size=16, max_blocks=16)) == UNSUP
+    assert _naive(m, _kv(), ws_bytes=16 * 128 * 512 * 2 - 1) == WS
