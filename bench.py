@@ -16,15 +16,23 @@ on) and the fp64 CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# the split-T kernel's sources: a traffic figure taken with hardware counters
+# holds only for the code it was taken on
+KERNEL_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_decode.hip",
+                  "head_latent_attention_mla_amd/csrc/mla_common.h",
+                  "head_latent_attention_mla_amd/csrc/mla_internal.h")
+COPY_BYTES = 1 << 30         # read (and written) by the copy-kernel calibration run
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 N_COPIES = 3
@@ -33,7 +41,8 @@ N_COPIES = 3
 def algorithmic_counts(B, s_q, H, seqlens, causal, cache_elem_bytes=2, scale_bytes=0):
     """FLOPs and bytes by the pages' counting rule: 2 per multiply-add over the
     causally visible (query, cached row) pairs, 2*576 + 2*512 per head and pair;
-    a cached row is read once."""
+    a cached row is read once, the latent query read once and the latent output
+    written once (split partials are implementation overhead, not counted)."""
     pairs = 0
     rows = 0
     for T in seqlens:
@@ -44,39 +53,87 @@ def algorithmic_counts(B, s_q, H, seqlens, causal, cache_elem_bytes=2, scale_byt
     f_absorb = 2 * (2 * B * s_q * H * 128 * 512)
     by_cache = rows * (576 * cache_elem_bytes + scale_bytes)
     by_qlat = B * s_q * H * 576 * 2
+    by_olat = B * s_q * H * 512 * 2        # the latent output at its narrowest width (bf16)
     by_weights = 2 * H * 128 * 512 * 2
     by_q, by_out = B * s_q * H * 192 * 2, B * s_q * H * 128 * 2
     return dict(flops_scan=f_scan, flops_step=f_scan + f_absorb,
-                bytes_scan=by_cache + by_qlat,
+                bytes_scan=by_cache + by_qlat + by_olat, bytes_cache=by_cache,
                 bytes_step=by_cache + by_weights + by_q + by_out)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the split-T kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None when there is none or the kernel has changed since."""
+    path = os.path.join(ROOT, "profiles", f"decode_split_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    if not t or not d or d.group(1) != kernel_source_digest():
+        return None
+    return int(t.group(1))
+
+
+def copy_calibration(steps: int):
+    """A plain elementwise copy of COPY_BYTES (fp32 negation, one read and one
+    write per element), the known-size kernel that scales the HBM counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.randn(COPY_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"calibration": "copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "us_per_launch": round(us, 2), "copy_gbs": round(2 * COPY_BYTES / us / 1e3, 1)}), flush=True)
 
 
 def cpu_baseline(inp, scale, seconds_target=15.0):
     """The fp64 oracle (naive expand-then-attend) on a bounded sample of (b, h)
-    pairs of the same workload, scaled to the step's metric."""
+    pairs of the same workload, scaled to the step's metric: the absorbed-path
+    FLOPs of the sampled pairs (the same counting rule as the GPU figure) per
+    second of oracle time."""
     import numpy as np
     from threadpoolctl import threadpool_info
     import oracle
 
     w = inp["workload"]
-    T = int(inp["seqlens"][0])
     rng = np.random.default_rng(0)
-    per_pair_flops = T * w.s_q * (2 * 576 + 2 * 512) + 2 * 2 * 128 * 512 * w.s_q
-    done, t0 = 0, time.perf_counter()
+    flops, done, t0 = 0, 0, time.perf_counter()
     while time.perf_counter() - t0 < seconds_target:
         pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
         oracle.naive_decode(inp, scale, pairs=pairs)
+        for b, _ in pairs:
+            T = int(inp["seqlens"][b])
+            vis = sum((T - w.s_q + j + 1) if w.causal else T for j in range(w.s_q))
+            flops += vis * (2 * 576 + 2 * 512) + 2 * 2 * 128 * 512 * w.s_q
         done += len(pairs)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
-        "value": done * per_pair_flops / dt / 1e12,
+        "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} (sequence, head) pairs of the B=64 H=128 T=4096 workload, fp64 numpy naive "
-                  f"expand-then-attend, {dt:.1f} s; value = absorbed-path FLOPs of those pairs per second",
-        "tokens_per_s": done / w.H / dt,
+        "sample": f"{done} random (sequence, head) pairs of the {w.name} workload (B={w.B} H={w.H} "
+                  f"s_q={w.s_q} T={w.T or w.T_range}), fp64 numpy naive expand-then-attend, {dt:.1f} s; "
+                  f"value = absorbed-path FLOPs of those pairs per second",
+        "tokens_per_s": done / w.H * w.s_q / dt,
     }
 
 
@@ -90,13 +147,22 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--naive-steps", type=int, default=3,
                     help="calls of the naive expand-then-attend ablation to time (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the known-size copy kernel that scales the HBM byte counters")
+    ap.add_argument("--kernel-digest", action="store_true", help="print the split-T kernel source digest")
     args = ap.parse_args()
+    if args.kernel_digest:
+        print(kernel_source_digest())
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
               "multi-GPU path; data-parallel attention would shard whole sequences per GPU.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    if args.calibrate_copy:
+        copy_calibration(max(args.steps, 1))
+        return
+
     import torch
     from head_latent_attention_mla_amd import workloads as W
     from head_latent_attention_mla_amd import mla
@@ -185,7 +251,7 @@ def main():
         "peak": HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS,
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
         "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / BF16_PEAK_TFLOPS), 4),
-        "traffic": None,
+        "traffic": measured_traffic(w.name),
         "algorithmic_bytes_per_launch": cnt["bytes_scan"],
         "algorithmic_flops_per_launch": cnt["flops_scan"],
         "avg_launch_us": round(kern_us["decode_split"], 2),
