@@ -3,8 +3,8 @@
 One step = the whole absorbed path over one batch of the DeepSeek-V3-shaped
 decode workload (B=64 sequences, H=128 heads, 4096 cached rows each in a
 contiguous bf16 latent cache [64, 4096, 576], one query token, seeded Gaussian
-inputs): absorb W_UK into the queries, scan the latent cache (split-T), merge
-the splits, project back through W_UV.  Inputs are resident in HBM before the
+inputs): absorb W_UK into the queries, scan the latent cache (split-T), then
+merge the splits and project back through W_UV in one fused pass.  Inputs are resident in HBM before the
 timed region; each step reads a different one of three cache copies so the
 256 MB last-level cache cannot serve a step from the previous one.
 
@@ -182,7 +182,6 @@ def main():
     B, s_q, H = w.B, w.s_q, w.H
     N = B * s_q
     q_lat = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=dev)
-    o_lat = torch.empty((B, s_q, H, 512), dtype=torch.float32, device=dev)
     out = torch.empty((B, s_q, H, 128), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(mla.decode_workspace_bytes(B, s_q, H, cache0.max_seqlen), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -197,12 +196,9 @@ def main():
         mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
-        mla.decode_combine(ws, B, s_q, H, c.max_seqlen, o_lat=o_lat)
+        mla.decode_combine_out(ws, w_uv, B, s_q, H, c.max_seqlen, out=out.view(N, H, -1))
         if ev is not None:
             ev[3].record(stream)
-        mla.absorb_out(o_lat.view(N, H, -1), w_uv, out=out.view(N, H, -1))
-        if ev is not None:
-            ev[4].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -221,15 +217,15 @@ def main():
 
     # per-kernel durations with HIP events on the launch stream (recorded
     # back to back, read after one synchronisation)
-    names = ["absorb_q", "decode_split", "decode_combine", "absorb_out"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    names = ["absorb_q", "decode_split", "combine_out"]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    tot = [0.0] * 4
+    tot = [0.0] * len(names)
     for i in range(args.steps):
-        for k in range(4):
+        for k in range(len(names)):
             tot[k] += evs[i][k].elapsed_time(evs[i][k + 1])
     kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
 

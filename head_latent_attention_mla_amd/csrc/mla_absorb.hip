@@ -49,8 +49,8 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
       if (!ok) a[ks] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
-  i16x8 abuf[2][D_NOPE / 16];
-  load_a(0, abuf[0]);
+  i16x8 abuf0[D_NOPE / 16], abuf1[D_NOPE / 16];
+  load_a(0, abuf0);
 
   // stage W_UK[h][0:128][cblk*128 : +128]
   {
@@ -85,9 +85,7 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     const int krow = ks * 16 + 8 * half + (jj >> 2);
     bw[ks] = join_tr(ds_read_tr16(wt + aq_off(krow, bcol)), ds_read_tr16(wt + aq_off(krow + 4, bcol)));
   }
-  for (int nb = 0; nb < nblocks; ++nb) {
-    i16x8(&a)[D_NOPE / 16] = abuf[nb & 1];
-    if (nb + 1 < nblocks) load_a(nb + 1, abuf[(nb + 1) & 1]);
+  auto block = [&](int nb, const i16x8 (&a)[D_NOPE / 16]) {
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D_NOPE / 16; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8, a[ks]), bw[ks], acc);
@@ -104,6 +102,15 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
       if (nn < N)
         *(i16x8*)(q_lat + ((int64_t)nn * H + h) * ROWW + cblk * AQ_COLS + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
     }
+  };
+  // two named fragment buffers, alternating (indexing an array of them by the
+  // block parity would place it in scratch memory)
+  for (int nb = 0; nb < nblocks; nb += 2) {
+    if (nb + 1 < nblocks) load_a(nb + 1, abuf1);
+    block(nb, abuf0);
+    if (nb + 1 >= nblocks) break;
+    if (nb + 2 < nblocks) load_a(nb + 2, abuf0);
+    block(nb + 1, abuf1);
   }
 }
 
@@ -220,7 +227,158 @@ __global__ __launch_bounds__(256) void absorb_out_kernel(const void* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// combine_out: the log-sum-exp merge of the split partials fused with the
+// projection through W_UV, so the latent output never round-trips through
+// HBM.  grid (H, ceil(N / 32)), 4 waves.  Per work-group: merge the partials
+// of 32 query rows of one head (the merge arithmetic is the one of the
+// stand-alone merge kernel, term for term), stage them as bf16 high + low
+// MFMA operands in LDS, then stream W_UV[h] through LDS in four 128-row
+// chunks; wave w computes output columns 32 w .. 32 w + 31.
+// ---------------------------------------------------------------------------
+constexpr int CO_ROWS = 32;
+constexpr int CO_KC = 128;                        // W_UV rows per staged chunk
+constexpr int CO_WBYTES = CO_KC * D_V * 2;        // 32 KB
+constexpr int CO_ABYTES = CO_ROWS * D_C * 2;      // one bf16 operand plane, 32 KB
+
+// row-major [32][512] bf16 operand plane; the 16-byte chunk index is XORed
+// with the row so that the 32 rows of an MFMA fragment read hit all banks
+__device__ __forceinline__ int co_aoff(int r, int k) {
+  return r * (D_C * 2) + (((k >> 3) ^ (r & 15)) << 4) + (k & 7) * 2;
+}
+
+__global__ __launch_bounds__(256) void combine_out_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          int s_q, int H, int N, int n_split,
+                                                          const uint16_t* __restrict__ w_uv,
+                                                          uint16_t* __restrict__ out, void* o_lat,
+                                                          int o_bf16, float* lse_out) {
+  __shared__ __attribute__((aligned(1024))) char wt[2][CO_WBYTES];
+  __shared__ __attribute__((aligned(1024))) char at[2][CO_ABYTES];   // [hi, lo]
+  const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int R = s_q * H;
+  const uint16_t* wsrc = w_uv + (int64_t)h * D_C * D_V;
+
+  auto issue_w = [&](int kc) {
+    char* dst = wt[kc & 1] + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < CO_KC * AQ_CHUNKS / 256; ++i) {
+      const int slot = i * 256 + wave * 64 + lane;
+      const int k = slot / AQ_CHUNKS;
+      const int cc = (slot % AQ_CHUNKS) ^ chunk_swz(k);
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc + (int64_t)(kc * CO_KC + k) * D_V + cc * 8),
+                                       (lds_void_t*)(dst + i * 256 * 16), 16, 0, 0);
+    }
+  };
+  issue_w(0);
+
+  // ---- merge: thread -> row r = tid / 8, columns 4 (tid % 8) + 32 i
+  {
+    const int r = tid >> 3, cq = (tid & 7) * 4;
+    const int n = n0 + r;
+    const bool ok = n < N;
+    const int b = ok ? n / s_q : 0;
+    const int row = ok ? (n - b * s_q) * H + h : 0;
+    const int64_t sb = (int64_t)b * n_split;
+    float mx = -INFINITY;
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(sb + s) * R + row]);
+    float wsum = 0.f;
+    f32x4 acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s) {
+      const float ls = part_lse[(sb + s) * R + row];
+      if (ls == -INFINITY) continue;
+      const float w = exp2f(ls - mx);
+      wsum += w;
+      const float* src = part_o + ((sb + s) * R + row) * D_C + cq;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] += w * *(const f32x4*)(src + 32 * i);
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f32x4 v = acc[i] * inv;
+      if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int k = cq + 32 * i;
+      if (ok && o_lat != nullptr) {
+        const int64_t o = ((int64_t)n * H + h) * D_C + k;
+        if (o_bf16) {
+          const uint64_t packed = (uint64_t)bf16_bits(to_bf16(v[0])) | ((uint64_t)bf16_bits(to_bf16(v[1])) << 16) |
+                                  ((uint64_t)bf16_bits(to_bf16(v[2])) << 32) |
+                                  ((uint64_t)bf16_bits(to_bf16(v[3])) << 48);
+          *(uint64_t*)((uint16_t*)o_lat + o) = packed;
+        } else {
+          *(f32x4*)((float*)o_lat + o) = v;
+        }
+      }
+      // the projection sees the latent output at the precision the caller
+      // asked for: bf16 as is, fp32 as high + low bf16 terms
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 bh = to_bf16(v[e]);
+        hi[e] = bf16_bits(bh);
+        lo[e] = o_bf16 ? (uint16_t)0 : bf16_bits(to_bf16(v[e] - (float)bh));
+      }
+      const uint64_t ph = (uint64_t)hi[0] | ((uint64_t)hi[1] << 16) | ((uint64_t)hi[2] << 32) | ((uint64_t)hi[3] << 48);
+      const uint64_t pl = (uint64_t)lo[0] | ((uint64_t)lo[1] << 16) | ((uint64_t)lo[2] << 32) | ((uint64_t)lo[3] << 48);
+      *(uint64_t*)(at[0] + co_aoff(r, k)) = ph;
+      *(uint64_t*)(at[1] + co_aoff(r, k)) = pl;
+    }
+    if (ok && lse_out != nullptr && (tid & 7) == 0)
+      lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
+  }
+
+  // ---- projection: out[32 rows][32 w ..] over 4 chunks of 128 latent rows
+  const int v0 = wave * 32;
+  const int grp = (lane >> 4) & 1, jj = lane & 15;
+  const int bcol = v0 + grp * 16 + 4 * (jj & 3);
+  f32x16 acc = f32x16{};
+  for (int kc = 0; kc < D_C / CO_KC; ++kc) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // chunk kc (and the merged operands) visible; chunk kc-1 consumed
+    if (kc + 1 < D_C / CO_KC) issue_w(kc + 1);
+    const char* w = wt[kc & 1];
+#pragma unroll
+    for (int ks = 0; ks < CO_KC / 16; ++ks) {
+      const int kg = kc * CO_KC + ks * 16 + half * 8;        // A columns of this lane
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *(const i16x8*)(at[0] + co_aoff(l32, kg)));
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, *(const i16x8*)(at[1] + co_aoff(l32, kg)));
+      const int krow = ks * 16 + 8 * half + (jj >> 2);
+      const bf16x8 bw = join_tr(ds_read_tr16(w + aq_off(krow, bcol)), ds_read_tr16(w + aq_off(krow + 4, bcol)));
+      acc = mfma32(ahi, bw, acc);
+      if (!o_bf16) acc = mfma32(alo, bw, acc);
+    }
+  }
+  // ---- stage the 32 x 128 output block, then write whole 256-byte rows
+  __syncthreads();
+  uint16_t(*ot)[D_V + 8] = (uint16_t(*)[D_V + 8])at[0];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ot[8 * (r >> 2) + 4 * half + (r & 3)][v0 + l32] = bf16_bits(to_bf16(acc[r]));
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = i * 256 + tid;   // 32 rows x 16 chunks of 16 B
+    const int rr = chunk >> 4, cc = chunk & 15;
+    const int n = n0 + rr;
+    if (n < N) *(i16x8*)(out + ((int64_t)n * H + h) * D_V + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_combine_out(const float* part_o, const float* part_lse, int B, int s_q, int H,
+                              int n_split, const uint16_t* w_uv, uint16_t* out, void* o_lat, int o_bf16,
+                              float* lse, hipStream_t stream) {
+  const int N = B * s_q;
+  hipLaunchKernelGGL(combine_out_kernel, dim3(H, (N + CO_ROWS - 1) / CO_ROWS), dim3(256), 0, stream, part_o,
+                     part_lse, s_q, H, N, n_split, w_uv, out, o_lat, o_bf16, lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_lat, int N, int H,
                            hipStream_t stream) {

@@ -177,6 +177,23 @@ mla_status mla_decode_combine(int32_t B, int32_t s_q, int32_t H, int32_t max_seq
                              o_lat_dtype, lse, (hipStream_t)stream);
 }
 
+mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                                  int32_t num_splits, const void* workspace, size_t ws_bytes,
+                                  const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
+                                  float* lse, void* stream) {
+  if (w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  Plan pl;
+  if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
+  if ((int64_t)B * s_q * H > (1 << 26)) return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
+  const float* part_o = (const float*)workspace;
+  const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
+  return hip_status(mla::launch_combine_out(part_o, part_lse, B, s_q, H, pl.n_split, (const uint16_t*)w_uv,
+                                            (uint16_t*)out, o_lat, o_lat_dtype == MLA_BF16, lse,
+                                            (hipStream_t)stream));
+}
+
 mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                            int32_t H, float softmax_scale, int32_t causal, void* o_lat,
                            int32_t o_lat_dtype, float* lse, void* workspace, size_t ws_bytes,

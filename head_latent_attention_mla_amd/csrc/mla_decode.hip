@@ -189,9 +189,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     if (PAGED) return (int64_t)p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)] * KT;
     return (int64_t)b * p.T_stride + ts;
   };
-  auto tile_rsrc = [&](int tile) {
+  // live = false gives an empty window: its loads fetch nothing and write zeros
+  auto tile_rsrc = [&](int tile, bool live) {
     const int ts = t_begin + tile * KT;
-    const int valid = min(KT, T - ts);
+    const int valid = live ? min(KT, T - ts) : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW * ELEM), (short)0,
                                              valid * ROWW * ELEM, 0x00020000);
   };
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   };
   constexpr int NLOADS = FP8 ? 9 : 18;         // 1 KB loads per wave per tile
   auto issue_tile = [&](int tile, int buf) {
-    const auto rsrc = tile_rsrc(tile);
+    const auto rsrc = tile_rsrc(tile, true);
     static_for<0, NLOADS>([&](auto kc) { issue_load(rsrc, buf, kc); });
   };
   // FP8: thread tid converts row tid / 4 of a tile, quarter tid % 4 (144 codes);
@@ -293,7 +294,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   for (int tile = 0; tile < n_tiles; ++tile) {
     barrier_tile_ready();   // tile ready; every wave is past the previous value phase
     const bool has_next = tile + 1 < n_tiles;
-    const auto next = tile_rsrc(has_next ? tile + 1 : tile);
+    // past the last tile the loads still run (no branch in the loop) but
+    // read an empty window into the idle buffer
+    const auto next = tile_rsrc(has_next ? tile + 1 : tile, has_next);
     const int next_buf = (tile + 1) & 1;
     uint32_t tb_a;
     if constexpr (FP8) {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
         // the next tile's loads ride along, one per two k-steps
         constexpr int every = FP8 ? 4 : 2;
         if constexpr (ks % every == 0 && ks / every < NLOADS) {
-          if (has_next) issue_load(next, next_buf, std::integral_constant<int, ks / every>{});
+          issue_load(next, next_buf, std::integral_constant<int, ks / every>{});
         }
         wait_lgkm<2 * ahead>(ra[ks & 3][0], ra[ks & 3][1]);
         const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[ks & 3][0]);
@@ -414,47 +417,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
         *(bf16x8*)(pbuf + ((wave * 4 + 2 * sb + j) * 64 + lane) * 16) = pk[sb][j];
 
     // ================= value phase (128 columns x all rows) =================
+    // 16 units u = 4 kap + cb, each 4 MFMAs (one per row block rb) sharing one
+    // transposed tile fragment A[u]; the probability fragments B[kap] of the
+    // 4 row blocks serve the 4 units of a kap.  A runs in a ring of three
+    // (issued two units ahead), B in two buffers (issued at unit cb = 2 of the
+    // previous kap); every wait names the exact number of younger LDS reads.
     {
       const uint32_t pa0 = tb_a + pvoff[0];
       const uint32_t pa1 = tb_a + pvoff[1];
       i16x8 bq[2][4];
-      i16x4 tr[2][4][2];
-      auto issue_tr = [&](auto kc) {
-        constexpr int kap = decltype(kc)::value;
-        constexpr int slot = kap & 1;
-        static_for<0, 4>([&](auto cbc) {
-          constexpr int cb = decltype(cbc)::value;
-          constexpr int off = 16 * kap * (CHUNKS * 16) + 128 * (cb >> 1);
-          const uint32_t a = (cb & 1) ? pa1 : pa0;
-          lds_read_tr16<off>(tr[slot][cb][0], a);
-          lds_read_tr16<off + 8 * CHUNKS * 16>(tr[slot][cb][1], a);
-        });
+      i16x4 tr[3][2];
+      auto issue_a = [&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int kap = u >> 2, cb = u & 3;
+        constexpr int off = 16 * kap * (CHUNKS * 16) + 128 * (cb >> 1);
+        const uint32_t a = (cb & 1) ? pa1 : pa0;
+        lds_read_tr16<off>(tr[u % 3][0], a);
+        lds_read_tr16<off + 8 * CHUNKS * 16>(tr[u % 3][1], a);
       };
-      auto issue_bq = [&](auto kc) {
+      auto issue_b = [&](auto kc) {
         constexpr int kap = decltype(kc)::value;
-        constexpr int slot = kap & 1;
         static_for<0, 4>([&](auto rbc) {
           constexpr int rb = decltype(rbc)::value;
-          lds_read_b128<(rb * 4 + kap) * 1024>(bq[slot][rb], pb_lane);
+          lds_read_b128<(rb * 4 + kap) * 1024>(bq[kap & 1][rb], pb_lane);
         });
-      };
-      auto issue_pv = [&](auto kc) {
-        issue_tr(kc);
-        issue_bq(kc);
       };
       // the first transposed tile reads only need the tile: issue them before
       // the barrier that publishes the probabilities
-      issue_tr(std::integral_constant<int, 0>{});
+      issue_a(std::integral_constant<int, 0>{});
+      issue_a(std::integral_constant<int, 1>{});
       barrier_lds();   // probabilities of all 128 rows visible
-      issue_bq(std::integral_constant<int, 0>{});
-      static_for<0, 4>([&](auto kc) {
-        constexpr int kap = decltype(kc)::value;
-        constexpr int slot = kap & 1;
-        wait_lgkm<0>(bq[slot][0], bq[slot][1], bq[slot][2], bq[slot][3],
-                     tr[slot][0][0], tr[slot][0][1], tr[slot][1][0], tr[slot][1][1],
-                     tr[slot][2][0], tr[slot][2][1], tr[slot][3][0], tr[slot][3][1]);
-        if constexpr (kap + 1 < 4) issue_pv(std::integral_constant<int, kap + 1>{});
-        if constexpr (kap == 0) {
+      issue_b(std::integral_constant<int, 0>{});
+      static_for<0, 16>([&](auto uc) {
+        constexpr int u = decltype(uc)::value;
+        constexpr int kap = u >> 2, cb = u & 3;
+        // reads issued after A[u] (and after B[kap] when cb == 0): A[u + 1]
+        // (2) unless it is the last unit, plus B[kap + 1] (4) when cb == 3
+        constexpr int younger = (u == 15 ? 0 : 2) + ((cb == 3 && kap < 3) ? 4 : 0) - (u == 0 ? 2 : 0);
+        if constexpr (cb == 0) {
+          wait_lgkm<younger>(tr[u % 3][0], tr[u % 3][1], bq[kap & 1][0], bq[kap & 1][1], bq[kap & 1][2],
+                             bq[kap & 1][3]);
+        } else {
+          wait_lgkm<younger>(tr[u % 3][0], tr[u % 3][1]);
+        }
+        if constexpr (u + 2 < 16) issue_a(std::integral_constant<int, u + 2>{});
+        if constexpr (cb == 2 && kap < 3) issue_b(std::integral_constant<int, kap + 1>{});
+        if constexpr (u == 0) {
           // reference steps of rows 32 rb + l32, carried in the sign bits of
           // the first three probabilities of the kappa = 0 fragment
           float alpha[4];
@@ -469,24 +477,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
           }
           if (__builtin_amdgcn_ballot_w64(any_step) != 0) {
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int c2 = 0; c2 < 4; ++c2)
 #pragma unroll
-              for (int rb = 0; rb < 4; ++rb) scale_acc(acc[cb][rb], alpha[rb]);
+              for (int rb = 0; rb < 4; ++rb) scale_acc(acc[c2][rb], alpha[rb]);
+          }
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            u32x4 v = __builtin_bit_cast(u32x4, bq[0][rb]);
+            v[0] &= 0x7FFF7FFFu;
+            v[1] &= 0x7FFF7FFFu;
+            bq[0][rb] = __builtin_bit_cast(i16x8, v);
           }
         }
-        bf16x8 bb[4];
+        const bf16x8 a = join_tr(tr[u % 3][0], tr[u % 3][1]);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          u32x4 v = __builtin_bit_cast(u32x4, bq[slot][rb]);
-          v &= 0x7FFF7FFFu;
-          bb[rb] = __builtin_bit_cast(bf16x8, v);
-        }
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const bf16x8 a = join_tr(tr[slot][cb][0], tr[slot][cb][1]);
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) acc[cb][rb] = mfma32(a, bb[rb], acc[cb][rb]);
-        }
+        for (int rb = 0; rb < 4; ++rb)
+          acc[cb][rb] = mfma32(a, __builtin_bit_cast(bf16x8, bq[kap & 1][rb]), acc[cb][rb]);
       });
     }
   }

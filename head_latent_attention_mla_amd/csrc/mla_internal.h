@@ -64,6 +64,9 @@ hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_
                            hipStream_t stream);
 hipError_t launch_absorb_out(const void* o_lat, int o_bf16, const uint16_t* w_uv, uint16_t* out,
                              int N, int H, hipStream_t stream);
+hipError_t launch_combine_out(const float* part_o, const float* part_lse, int B, int s_q, int H,
+                              int n_split, const uint16_t* w_uv, uint16_t* out, void* o_lat, int o_bf16,
+                              float* lse, hipStream_t stream);
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -60,6 +60,7 @@ SIGNATURES = {
                                   _VP]),
     "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
     "mla_absorb_out": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
+    "mla_decode_combine_out": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, _I32, _VP, _VP]),
     "mla_naive_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_naive_decode": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP,
                                 _VP, _SZ, _VP]),
@@ -244,6 +245,26 @@ def decode_combine(workspace: torch.Tensor, B: int, s_q: int, H: int, max_seqlen
     return o_lat, lse
 
 
+def decode_combine_out(workspace: torch.Tensor, w_uv: torch.Tensor, B: int, s_q: int, H: int, max_seqlen: int,
+                       num_splits: int = 0, o_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+                       o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+    """Phases 2 + 4 fused: merge the split partials and project through W_UV.
+    Returns out [B * s_q, H, 128] bf16; o_lat and lse are written when given."""
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
+    _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    if out is None:
+        out = torch.empty((B * s_q, H, D_V), dtype=torch.bfloat16, device=workspace.device)
+    _require(out, "out", torch.bfloat16, (B * s_q, H, D_V))
+    if o_lat is not None:
+        _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, s_q, H))
+    _check(_lib.mla_decode_combine_out(B, s_q, H, max_seqlen, num_splits, _ptr(workspace), workspace.numel(),
+                                       _ptr(w_uv), _ptr(out), _ptr(o_lat), dt, _ptr(lse), _stream(stream)),
+           "mla_decode_combine_out")
+    return out
+
+
 def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """o_lat [N, H, 512] (fp32 or bf16), W_UV [H, 512, 128] bf16 -> out [N, H, 128] bf16."""
     N, H = o_lat.shape[0], o_lat.shape[1]
@@ -260,10 +281,16 @@ def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
 
 def decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
            scale: float = DEFAULT_SCALE, causal: bool = False, o_dtype=torch.float32,
-           num_splits: int = 0, stream=None) -> torch.Tensor:
-    """Absorbed MLA decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16."""
+           num_splits: int = 0, fused: bool = True, stream=None) -> torch.Tensor:
+    """Absorbed MLA decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16.
+    fused: merge and project in one pass (mla_decode_combine_out); otherwise
+    mla_decode_attn then mla_absorb_out.  Both give the same bits."""
     B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
     q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
+    if fused:
+        ws = decode_partial(q_lat, cache, scale, causal, num_splits, stream=stream)
+        out = decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, num_splits, o_dtype, stream=stream)
+        return out.view(B, s_q, H, D_V)
     o_lat, _ = decode_attn(q_lat, cache, scale, causal, o_dtype, num_splits, want_lse=False, stream=stream)
     return absorb_out(o_lat.view(B * s_q, H, D_C), w_uv, stream=stream).view(B, s_q, H, D_V)
 

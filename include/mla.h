@@ -191,6 +191,25 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
                           void* out, int32_t N, int32_t H, int32_t d_c,
                           int32_t d_v, void* stream);
 
+/* Steps 3 + 4 fused -- merge the split partials and project back per head in
+ * one pass, so the latent output is not written to and re-read from memory
+ * (the value order of "MLA, dim by dim", "MLA Decode": the latent output of
+ * each head goes straight through W_UV[h]).  The result is bitwise equal to
+ * mla_decode_combine followed by mla_absorb_out with the same o_lat_dtype.
+ *   B, s_q, H, max_seqlen, num_splits, workspace, ws_bytes: as given to
+ *          mla_decode_partial (the workspace holds its partials).
+ *   w_uv   bf16 [H, 512, 128]
+ *   out    bf16 [B * s_q, H, 128]
+ *   o_lat  NULL, or [B, s_q, H, 512] of o_lat_dtype: also written when given.
+ *   o_lat_dtype  MLA_FP32 (the latent output enters the projection as high +
+ *          low bf16 terms) or MLA_BF16 (rounded to bf16 first), whether or not
+ *          o_lat is written.
+ *   lse    NULL or fp32 [B, s_q, H], natural log. */
+mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                                  int32_t num_splits, const void* workspace, size_t ws_bytes,
+                                  const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
+                                  float* lse, void* stream);
+
 /* Ablation only -- the naive up-project-then-attend form ("The MLA decode
  * speedup hiding in your model card", "The naive form, written out"; "Why MLA
  * and MTP Fight Each Other", section 5.1, expand bracketing).  Every visible

@@ -140,3 +140,14 @@ def test_naive_rejects_bad_arguments(m):
     assert _naive(m, _kv(max_seqlen=8), s_q=5) == UNSUP     # at most 4 query tokens
     assert _naive(m, _kv(block_table=0x7000, block_size=16, max_blocks=16)) == UNSUP
     assert _naive(m, _kv(), ws_bytes=16 * 128 * 512 * 2 - 1) == WS
+
+
+def test_combine_out_rejects_bad_arguments(m):
+    co = m._lib.mla_decode_combine_out
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    assert co(2, 1, 16, 256, 0, 0x1000, need, None, 0x2000, None, 2, None, None) == ARG     # no w_uv
+    assert co(2, 1, 16, 256, 0, 0x1000, need, 0x3000, None, None, 2, None, None) == ARG     # no out
+    assert co(2, 1, 16, 256, 0, 0x1000, need, 0x3000, 0x2000, None, 1, None, None) == ARG   # fp8 o_lat
+    assert co(0, 1, 16, 256, 0, 0x1000, need, 0x3000, 0x2000, None, 2, None, None) == ARG
+    assert co(2, 1, 16, 256, 0, 0x1000, need - 1, 0x3000, 0x2000, None, 2, None, None) == WS
+    assert co(2, 1, 16, 256, 0, None, need, 0x3000, 0x2000, None, 2, None, None) == WS
