@@ -249,7 +249,9 @@ __device__ __forceinline__ int co_aoff(int r, int k) {
 
 __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
-                                                          int s_q, int H, int N, int n_split,
+                                                          const int32_t* __restrict__ seg_first,
+                                                          const int32_t* __restrict__ seg_count,
+                                                          int s_q, int H, int N,
                                                           const uint16_t* __restrict__ w_uv,
                                                           uint16_t* __restrict__ out, void* o_lat,
                                                           int o_bf16, float* lse_out) {
@@ -275,20 +277,24 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
   };
   issue_w(0);
 
-  // ---- merge: thread -> row r = tid / 8, columns 4 (tid % 8) + 32 i
-  {
-    const int r = tid >> 3, cq = (tid & 7) * 4;
+  // ---- merge: thread -> row r = tid / TPR, columns 4 (tid % TPR) + 4 TPR i;
+  // fewer rows in the block get more threads each (TPR = 8, 16 or 32)
+  auto merge = [&](auto tprc) {
+    constexpr int TPR = decltype(tprc)::value;
+    constexpr int NCH = D_C / 4 / TPR;       // 16-byte column chunks per thread
+    const int r = tid / TPR, cq = (tid % TPR) * 4;
     const int n = n0 + r;
-    const bool ok = n < N;
+    const bool ok = r < CO_ROWS && n < N;
     const int b = ok ? n / s_q : 0;
     const int row = ok ? (n - b * s_q) * H + h : 0;
-    const int64_t sb = (int64_t)b * n_split;
+    const int64_t sb = seg_first[b];
+    const int n_split = seg_count[b];
     float mx = -INFINITY;
     for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(sb + s) * R + row]);
     float wsum = 0.f;
-    f32x4 acc[16];
+    f32x4 acc[NCH];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n_split; ++s) {
       const float ls = part_lse[(sb + s) * R + row];
       if (ls == -INFINITY) continue;
@@ -296,14 +302,15 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
       wsum += w;
       const float* src = part_o + ((sb + s) * R + row) * D_C + cq;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[i] += w * *(const f32x4*)(src + 32 * i);
+      for (int i = 0; i < NCH; ++i) acc[i] += w * *(const f32x4*)(src + 4 * TPR * i);
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    if (r >= CO_ROWS) return;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       f32x4 v = acc[i] * inv;
       if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int k = cq + 32 * i;
+      const int k = cq + 4 * TPR * i;
       if (ok && o_lat != nullptr) {
         const int64_t o = ((int64_t)n * H + h) * D_C + k;
         if (o_bf16) {
@@ -329,8 +336,14 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
       *(uint64_t*)(at[0] + co_aoff(r, k)) = ph;
       *(uint64_t*)(at[1] + co_aoff(r, k)) = pl;
     }
-    if (ok && lse_out != nullptr && (tid & 7) == 0)
+    if (ok && lse_out != nullptr && (tid % TPR) == 0)
       lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
+  };
+  {
+    const int rows_here = min(CO_ROWS, N - n0);
+    if (rows_here > 16) merge(std::integral_constant<int, 8>{});
+    else if (rows_here > 8) merge(std::integral_constant<int, 16>{});
+    else merge(std::integral_constant<int, 32>{});
   }
 
   // ---- projection: out[32 rows][32 w ..] over 4 chunks of 128 latent rows
@@ -371,12 +384,12 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_combine_out(const float* part_o, const float* part_lse, int B, int s_q, int H,
-                              int n_split, const uint16_t* w_uv, uint16_t* out, void* o_lat, int o_bf16,
-                              float* lse, hipStream_t stream) {
+hipError_t launch_combine_out(const float* part_o, const float* part_lse, const int32_t* seg_first,
+                              const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
+                              uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
   const int N = B * s_q;
   hipLaunchKernelGGL(combine_out_kernel, dim3(H, (N + CO_ROWS - 1) / CO_ROWS), dim3(256), 0, stream, part_o,
-                     part_lse, s_q, H, N, n_split, w_uv, out, o_lat, o_bf16, lse);
+                     part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
   return hipGetLastError();
 }
 

@@ -19,12 +19,17 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int32_t R, n_groups, n_split, split_rows, n_work, work_per_xcd;
-  size_t part_o_bytes, part_lse_bytes, ws_bytes;
+  int32_t R, n_groups, n_split, n_ranges, n_work, work_per_xcd;
+  int64_t n_slots;
+  size_t part_o_bytes, part_lse_bytes, seg_bytes, ws_bytes;
 };
 
-// The split plan depends on host integers only, so the workspace size and the
-// reduction order are fixed for a given argument set.
+// The plan depends on host integers only, so the workspace size and the
+// reduction order are fixed for a given argument set.  n_split is the number
+// of parts a sequence of max_seqlen rows is scanned in; the device cuts the
+// tiles of all sequences into n_ranges = B * n_split equal ranges, so shorter
+// sequences get proportionally fewer parts.  A range covers at most one part
+// per sequence it touches: at most n_ranges + B partial slots.
 bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t forced, Plan* pl) {
   if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || forced < 0) return false;
   const int64_t R = (int64_t)s_q * H;
@@ -36,17 +41,18 @@ bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t fo
   int64_t ns = forced > 0 ? forced : (kTargetWorkGroups + base - 1) / base;
   if (ns < 1) ns = 1;
   if (ns > tiles) ns = tiles;
-  const int64_t split_tiles = (tiles + ns - 1) / ns;
-  ns = (tiles + split_tiles - 1) / split_tiles;
   pl->n_split = (int32_t)ns;
-  pl->split_rows = (int32_t)(split_tiles * kTileRows);
-  const int64_t n_work = base * ns;
+  const int64_t n_ranges = (int64_t)B * ns;
+  pl->n_slots = n_ranges + B;
+  const int64_t n_work = pl->n_slots * pl->n_groups;   // one work-group per (slot, row group)
   if (n_work > (int64_t)1 << 30) return false;
+  pl->n_ranges = (int32_t)n_ranges;
   pl->n_work = (int32_t)n_work;
   pl->work_per_xcd = (int32_t)((n_work + 7) / 8);
-  pl->part_o_bytes = align_up((size_t)B * R * ns * mla::D_C * sizeof(float));
-  pl->part_lse_bytes = align_up((size_t)B * R * ns * sizeof(float));
-  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes;
+  pl->part_o_bytes = align_up((size_t)pl->n_slots * R * mla::D_C * sizeof(float));
+  pl->part_lse_bytes = align_up((size_t)pl->n_slots * R * sizeof(float));
+  pl->seg_bytes = align_up((size_t)2 * B * sizeof(int32_t));
+  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes + pl->seg_bytes;
   return true;
 }
 
@@ -129,6 +135,8 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   p.seqlens = kv->seqlens;
   p.part_o = (float*)workspace;
   p.part_lse = (float*)((char*)workspace + pl.part_o_bytes);
+  p.seg_first = (int32_t*)((char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
+  p.seg_count = p.seg_first + B;
   p.T_stride = kv->T_stride;
   p.max_blocks = kv->max_blocks;
   p.B = B;
@@ -136,8 +144,7 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   p.H = H;
   p.R = pl.R;
   p.n_groups = pl.n_groups;
-  p.n_split = pl.n_split;
-  p.split_rows = pl.split_rows;
+  p.n_ranges = pl.n_ranges;
   p.n_work = pl.n_work;
   p.work_per_xcd = pl.work_per_xcd;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -157,7 +164,8 @@ mla_status decode_combine_impl(int32_t B, int32_t s_q, int32_t H, int32_t max_se
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
   const float* part_o = (const float*)workspace;
   const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
-  return hip_status(mla::launch_combine(part_o, part_lse, B, pl.R, pl.n_split, o_lat,
+  const int32_t* seg_first = (const int32_t*)((const char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
+  return hip_status(mla::launch_combine(part_o, part_lse, seg_first, seg_first + B, B, pl.R, o_lat,
                                         o_lat_dtype == MLA_BF16, lse, st));
 }
 
@@ -189,9 +197,10 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
   const float* part_o = (const float*)workspace;
   const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
-  return hip_status(mla::launch_combine_out(part_o, part_lse, B, s_q, H, pl.n_split, (const uint16_t*)w_uv,
-                                            (uint16_t*)out, o_lat, o_lat_dtype == MLA_BF16, lse,
-                                            (hipStream_t)stream));
+  const int32_t* seg_first = (const int32_t*)((const char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
+  return hip_status(mla::launch_combine_out(part_o, part_lse, seg_first, seg_first + B, B, s_q, H,
+                                            (const uint16_t*)w_uv, (uint16_t*)out, o_lat,
+                                            o_lat_dtype == MLA_BF16, lse, (hipStream_t)stream));
 }
 
 mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,

@@ -28,9 +28,11 @@
 // of three of the row's probabilities (always >= 0 otherwise), and every wave
 // multiplies that row's accumulators by 2^(-64 k).
 //
-// The cache is split along T into n_split ranges; each (sequence, range, row
-// group) is one work-group writing a normalised partial output row per query
-// row and its log2-domain log-sum-exp.  The combine kernel merges the ranges.
+// Work is balanced over ragged lengths: the 64-row tiles of all sequences are
+// cut into equal ranges; each (range, row group) is one work-group, which
+// writes, per sequence segment it covers, a normalised partial output row per
+// query row and its log2-domain log-sum-exp.  The merge kernels combine the
+// parts of each sequence.
 #include "mla_common.h"
 #include "mla_internal.h"
 
@@ -50,6 +52,22 @@ static_assert(2 * TILE_BYTES + P_BYTES <= 160 * 1024, "LDS budget");
 __device__ __forceinline__ int lds_off(int t, int elem) {
   const int c = elem >> 3;
   return (t * CHUNKS + (c ^ chunk_swz(t))) * 16 + (elem & 7) * 2;
+}
+
+// floor(a / b) for 0 <= a < 2^62, 0 < b: a double estimate corrected with
+// exact integer products (cheaper than the 64-bit division routine).
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = (int64_t)((double)a / (double)b);
+  while (q > 0 && q * b > a) --q;
+  while ((q + 1) * b <= a) ++q;
+  return q;
+}
+
+// A value every lane holds alike, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Work-group barriers that wait only for what the barrier publishes.
@@ -127,25 +145,92 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   const uint32_t smem_a = lds_addr(smem);
   const uint32_t pbuf_a = smem_a + 2 * TILE_BYTES;
 
-  // blockIdx -> work item: consecutive work items (the row groups and splits
-  // of one sequence) go to the same XCD, whose L2 they share.
-  const int xcd = blockIdx.x % 8;
-  const int w_item = xcd * p.work_per_xcd + blockIdx.x / 8;
-  if (w_item >= p.n_work) return;
-  const int g = w_item % p.n_groups;
-  const int bsplit = w_item / p.n_groups;
-  const int split = bsplit % p.n_split;
-  const int b = bsplit / p.n_split;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
+  // ---- the work plan.  Sequence b (n_t tiles of 64 rows, N tiles in all)
+  // is scanned in parts(b) = clamp(n_t * n_ranges / N, 1, n_t) nearly equal parts,
+  // so the work per part is about the same for every sequence (and exactly
+  // n_ranges / B parts each when all lengths are equal).  Its parts take the
+  // partial slots Qp[b] .. Qp[b] + parts(b) - 1 (Qp: prefix sum of parts),
+  // fewer than n_ranges + B in all.  Every work-group derives the same plan
+  // from the sequence lengths (chunked sums and two inclusive scans over the
+  // 256 chunks), then takes one (slot, row group) pair; the blockIdx -> pair
+  // map puts consecutive slots on one XCD (shared L2) and the surplus
+  // work-groups of the launch at its end.
+  int b, j, parts;
+  int sl;
+  int g;
+  {
+    int64_t* scan = (int64_t*)pbuf;        // 2 x 256 entries; the probability buffer is idle here
+    int64_t* found = scan + 2 * NTHREADS;  // the slot's sequence and its first slot
+    const int chunk = (p.B + NTHREADS - 1) / NTHREADS;
+    const int c0 = min(p.B, tid * chunk), c1 = min(p.B, c0 + chunk);
+    // inclusive prefix over the 256 threads: shuffle scan within each wave,
+    // then the wave totals through LDS; found[2] receives the grand total
+    auto inclusive_scan = [&](int64_t mine) -> int64_t {
+      int64_t v = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int64_t u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+      }
+      if (lane == 63) scan[wave] = v;
+      __syncthreads();
+      int64_t before = 0;
+      for (int w2 = 0; w2 < wave; ++w2) before += scan[w2];
+      const int64_t all = scan[0] + scan[1] + scan[2] + scan[3];
+      __syncthreads();
+      found[2] = all;
+      return v + before;
+    };
+    int64_t tiles_mine = 0;
+    for (int bb = c0; bb < c1; ++bb) tiles_mine += (p.seqlens[bb] + KT - 1) / KT;
+    (void)inclusive_scan(tiles_mine);
+    const int64_t total = uniform64(found[2]);
+    auto parts_of = [&](int bb) -> int {     // in [1, n_t]: every part holds a tile
+      const int64_t nt = (p.seqlens[bb] + KT - 1) / KT;
+      const int64_t q = floor_div(nt * p.n_ranges, total);
+      return (int)(q < 1 ? 1 : (q > nt ? nt : q));
+    };
+    int64_t parts_mine = 0;
+    for (int bb = c0; bb < c1; ++bb) parts_mine += parts_of(bb);
+    const int64_t pincl = inclusive_scan(parts_mine);
+    const int n_slots = (int)uniform64(found[2]);
+    const int n_real = n_slots * p.n_groups;
+    const int per_xcd = (n_real + 7) / 8;
+    const int w_item = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (w_item >= n_real || blockIdx.x / 8 >= per_xcd) return;   // surplus (uniform per work-group)
+    g = w_item % p.n_groups;
+    sl = w_item / p.n_groups;
+    if (pincl - parts_mine <= sl && sl < pincl) {
+      int bb = c0;
+      int64_t q = pincl - parts_mine;
+      while (q + parts_of(bb) <= sl) {
+        q += parts_of(bb);
+        ++bb;
+      }
+      found[0] = bb;
+      found[1] = q;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane((int)found[0]);
+    const int q0 = __builtin_amdgcn_readfirstlane((int)found[1]);
+    __syncthreads();                       // the buffer is reused below
+    parts = parts_of(b);
+    j = sl - q0;
+    if (g == 0 && tid == 0 && j == 0) {    // where sequence b's partials are
+      p.seg_first[b] = q0;
+      p.seg_count[b] = parts;
+    }
+  }
+  const int nt_b = (p.seqlens[b] + KT - 1) / KT;
   const int T = p.seqlens[b];
-  const int t_begin = split * p.split_rows;
-  const int t_end = min(T, t_begin + p.split_rows);
+  const int t_begin = (int)floor_div((int64_t)j * nt_b, parts) * KT;
+  const int t_end = min(T, (int)floor_div((int64_t)(j + 1) * nt_b, parts) * KT);
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + KT - 1) / KT : 0;
 
   // ---- rows owned by this wave for the score phase
@@ -319,25 +404,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       uint32_t qa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) qa[i] = tb_a + qoff[i];
-      i16x8 ra[4][2];
+      constexpr int QK_AHEAD = 3;              // k-steps of A fragments in flight
+      i16x8 ra[QK_AHEAD + 1][2];
       auto issue_qk = [&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
-        lds_read_b128<128 * (ks >> 2)>(ra[ks & 3][0], qa[ks & 3]);
-        lds_read_b128<128 * (ks >> 2) + 32 * CHUNKS * 16>(ra[ks & 3][1], qa[ks & 3]);
+        lds_read_b128<128 * (ks >> 2)>(ra[ks % (QK_AHEAD + 1)][0], qa[ks & 3]);
+        lds_read_b128<128 * (ks >> 2) + 32 * CHUNKS * 16>(ra[ks % (QK_AHEAD + 1)][1], qa[ks & 3]);
       };
-      static_for<0, 3>(issue_qk);
+      static_for<0, QK_AHEAD>(issue_qk);
       static_for<0, ROWW / 16>([&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
-        constexpr int ahead = (ROWW / 16 - 1 - ks) < 3 ? (ROWW / 16 - 1 - ks) : 3;
-        if constexpr (ks + 3 < ROWW / 16) issue_qk(std::integral_constant<int, ks + 3>{});
+        constexpr int ahead = (ROWW / 16 - 1 - ks) < QK_AHEAD ? (ROWW / 16 - 1 - ks) : QK_AHEAD;
+        if constexpr (ks + QK_AHEAD < ROWW / 16) issue_qk(std::integral_constant<int, ks + QK_AHEAD>{});
         // the next tile's loads ride along, one per two k-steps
         constexpr int every = FP8 ? 4 : 2;
         if constexpr (ks % every == 0 && ks / every < NLOADS) {
           issue_load(next, next_buf, std::integral_constant<int, ks / every>{});
         }
-        wait_lgkm<2 * ahead>(ra[ks & 3][0], ra[ks & 3][1]);
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[ks & 3][0]);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[ks & 3][1]);
+        constexpr int slot = ks % (QK_AHEAD + 1);
+        wait_lgkm<2 * ahead>(ra[slot][0], ra[slot][1]);
+        const bf16x8 a0 = __builtin_bit_cast(bf16x8, ra[slot][0]);
+        const bf16x8 a1 = __builtin_bit_cast(bf16x8, ra[slot][1]);
         if constexpr (ks == 0) {
           mfma32_v0(s0, a0, qf[ks]);
           mfma32_v0(s1, a1, qf[ks]);
@@ -345,6 +432,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
           mfma32_v(s0, a0, qf[ks]);
           mfma32_v(s1, a1, qf[ks]);
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep the k-step's waits, reads and MFMAs in order
       });
       mfma_v_drain(s0, s1);
 
@@ -357,16 +445,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
           s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
         }
       }
-      // running maximum on raw scores (the scale is positive)
-      float mraw = max3f(s0[0], s0[1], s1[0]);
-      mraw = max3f(mraw, s1[1], s0[2]);
+      // running maximum on raw scores (the scale is positive): four
+      // independent chains, then their maximum
+      float mq[4];
 #pragma unroll
-      for (int r = 2; r < 14; r += 2) {
-        mraw = max3f(mraw, s1[r], s0[r + 1]);
-        mraw = max3f(mraw, s1[r + 1], s0[r + 2]);
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * c;
+        float m = max3f(s0[r], s0[r + 1], s0[r + 2]);
+        m = max3f(m, s0[r + 3], s1[r]);
+        mq[c] = max3f(m, s1[r + 1], fmaxf(s1[r + 2], s1[r + 3]));
       }
-      mraw = max3f(mraw, s1[14], s0[15]);
-      mraw = fmaxf(mraw, s1[15]);
+      const float mraw = fmaxf(max3f(mq[0], mq[1], mq[2]), mq[3]);
       const float mx = max_halves(mraw) * p.scale_log2;
       // reference update, branch-free: the first visible scores set it; later
       // it moves up in steps of REF_STEP only when the maximum passes it by more
@@ -382,8 +471,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
         pk[0][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
         pk[1][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
       }
-      // row sum of the rounded probabilities, two at a time
-      float ls = 0.f;
+      // row sum of the rounded probabilities, two at a time in four chains
+      float lq[4] = {0.f, 0.f, 0.f, 0.f};
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -392,9 +481,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const bf16x2 pr = {pk[sb][j][e], pk[sb][j][e + 1]};
-            ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);
+            lq[2 * j + sb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq[2 * j + sb], false);
           }
-      l_sum += sum_halves(ls);
+      l_sum += sum_halves((lq[0] + lq[1]) + (lq[2] + lq[3]));
       if (kstep != 0) {
         // sign bits of the fragment's first three probabilities carry the
         // reference step (both lane halves, so every reader lane sees it)
@@ -493,6 +582,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
           acc[cb][rb] = mfma32(a, __builtin_bit_cast(bf16x8, bq[kap & 1][rb]), acc[cb][rb]);
+        __builtin_amdgcn_sched_barrier(0);   // a unit's MFMAs stay ahead of the next unit's wait
       });
     }
   }
@@ -503,9 +593,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   if (half == 0) lsh[wave * 32 + l32] = l_sum;
   barrier_lds();
 
-  // partial rows are row-major [B][n_split][R][512]: a lane pair covers 128
+  // partial rows are row-major [slot][R][512], slot = k + b (unique: along
+  // the plan, k and b never both stay put); a lane pair covers 128
   // contiguous bytes of one row per (cb, rb), stored back to back
-  const int64_t pbase = ((int64_t)b * p.n_split + split) * p.R;
+  const int64_t pbase = (int64_t)sl * p.R;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
     const int row = g * 128 + rb * 32 + l32;
@@ -523,35 +614,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       }
     }
   }
-  if (half == 0 && own_ok)
-    p.part_lse[((int64_t)b * p.n_split + split) * p.R + own_r] =
-        l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
+  if (half == 0 && own_ok) p.part_lse[pbase + own_r] = l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
 }
 
-// Merge the split partials of each query row: weights 2^(lse_s - max_s),
-// then the weighted mean of the normalised partial rows.  One thread per
-// (row, 4 latent columns); partial and output rows are contiguous, so every
-// load and store is coalesced.
+// Merge the partials of each query row: the parts of sequence b sit in
+// slots seg_first[b] .. seg_first[b] + seg_count[b] - 1; weights
+// 2^(lse_s - max_s), then the weighted mean of the normalised partial rows.
+// One thread per (row, 4 latent columns); partial and output rows are
+// contiguous, so every load and store is coalesced.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
-                                                      int B, int R, int n_split,
+                                                      const int32_t* __restrict__ seg_first,
+                                                      const int32_t* __restrict__ seg_count, int B, int R,
                                                       void* o_lat, int o_bf16, float* lse_out) {
   const int64_t row_g = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);   // b * R + row
   if (row_g >= (int64_t)B * R) return;
   const int b = (int)(row_g / R);
   const int row = (int)(row_g - (int64_t)b * R);
   const int c4 = (threadIdx.x & 127) * 4;
-  const int64_t sb = (int64_t)b * n_split;
+  const int64_t s0 = seg_first[b];
+  const int ns = seg_count[b];
   float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(sb + s) * R + row]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(s0 + s) * R + row]);
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < n_split; ++s) {
-    const float ls = part_lse[(sb + s) * R + row];
+  for (int s = 0; s < ns; ++s) {
+    const float ls = part_lse[(s0 + s) * R + row];
     if (ls == -INFINITY) continue;
     const float w = exp2f(ls - mx);
     wsum += w;
-    acc += w * *(const f32x4*)(part_o + ((sb + s) * R + row) * D_C + c4);
+    acc += w * *(const f32x4*)(part_o + ((s0 + s) * R + row) * D_C + c4);
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   acc *= inv;
@@ -586,11 +678,12 @@ hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int R, int n_split,
-                          void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
+hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
+                          const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,
+                          hipStream_t stream) {
   const int64_t rows = (int64_t)B * R;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, part_o, part_lse,
-                     B, R, n_split, o_lat, o_bf16, lse);
+                     seg_first, seg_count, B, R, o_lat, o_bf16, lse);
   return hipGetLastError();
 }
 

@@ -23,14 +23,16 @@ struct DecodeParams {
   const float* row_scale;       // e4m3 only
   const int32_t* block_table;   // paged only
   const int32_t* seqlens;       // [B]
-  float* part_o;                // fp32 [B, n_split, R, 512], normalised partial outputs
-  float* part_lse;              // fp32 [B, n_split, R], log2-domain log-sum-exp
+  float* part_o;                // fp32 [n_ranges + B, R, 512], normalised partial outputs
+  float* part_lse;              // fp32 [n_ranges + B, R], log2-domain log-sum-exp
+  int32_t* seg_first;           // [B] first partial slot of each sequence
+  int32_t* seg_count;           // [B] number of partial slots of each sequence
   int64_t T_stride;
   int32_t max_blocks;
   int32_t B, s_q, H, R;
   int32_t n_groups;             // ceil(R / 128) row groups per sequence
-  int32_t n_split, split_rows;  // split_rows is a multiple of 64
-  int32_t n_work, work_per_xcd; // B * n_split * n_groups work items over 8 XCDs
+  int32_t n_ranges;             // equal ranges of the tiles of all sequences
+  int32_t n_work, work_per_xcd; // n_ranges * n_groups work items over 8 XCDs
   float scale_log2;             // softmax scale * log2(e)
   int32_t causal;
   int32_t paged;
@@ -58,15 +60,16 @@ struct NaiveParams {
 constexpr int NAIVE_MAX_SQ = 4;
 
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_combine(const float* part_o, const float* part_lse, int B, int R, int n_split,
-                          void* o_lat, int o_bf16, float* lse, hipStream_t stream);
+hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
+                          const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,
+                          hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_lat, int N, int H,
                            hipStream_t stream);
 hipError_t launch_absorb_out(const void* o_lat, int o_bf16, const uint16_t* w_uv, uint16_t* out,
                              int N, int H, hipStream_t stream);
-hipError_t launch_combine_out(const float* part_o, const float* part_lse, int B, int s_q, int H,
-                              int n_split, const uint16_t* w_uv, uint16_t* out, void* o_lat, int o_bf16,
-                              float* lse, hipStream_t stream);
+hipError_t launch_combine_out(const float* part_o, const float* part_lse, const int32_t* seg_first,
+                              const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
+                              uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream);
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);
 
 }  // namespace mla

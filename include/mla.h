@@ -109,13 +109,14 @@ mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_lat,
                         int32_t d_c, void* stream);
 
 /* Bytes of device workspace mla_decode_attn needs for these sizes.
- * num_splits: 0 lets the library choose the split count; a positive value
- * forces it (any count gives the same result up to rounding).  Returns 0 for
- * invalid sizes. */
+ * num_splits: the number of parts a sequence of max_seqlen rows is scanned
+ * in; 0 lets the library choose, a positive value forces it (any count gives
+ * the same result up to rounding; it is capped at ceil(max_seqlen / 64)).
+ * Returns 0 for invalid sizes. */
 size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H,
                                   int32_t max_seqlen, int32_t num_splits);
 
-/* The split count mla_decode_attn will use for these sizes (host integers only). */
+/* The split count S mla_decode_attn will use for these sizes (host integers only). */
 int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H,
                               int32_t max_seqlen, int32_t num_splits);
 
@@ -131,10 +132,13 @@ int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H,
  * The causal rule (the s_q newest rows are the query tokens themselves, each
  * seeing itself and earlier rows) is this library's reading of speculative
  * verification of s_q tokens ("Why MLA and MTP Fight Each Other", section 8).
- * The cache is scanned in num_splits ranges of rows in parallel (split-T
- * flash decode), each range producing a partial normalised output and its
- * log-sum-exp in the workspace; a second kernel merges them with
- * log-sum-exp weights.
+ * The cache is scanned in parallel parts (split-T flash decode): the 64-row
+ * tiles of all sequences, in sequence order, are cut into B * S equal ranges
+ * (S = mla_decode_num_splits(...)), so work is balanced over ragged lengths
+ * and a sequence of max_seqlen rows gets S parts.  Each part (the piece of
+ * one sequence inside one range) produces a normalised partial output and its
+ * log-sum-exp in the workspace; a second kernel merges each sequence's parts
+ * with log-sum-exp weights.
  * q_lat        bf16 [B, s_q, H, 576]
  * kv           host pointer to the cache description (read during the call only)
  * o_lat        [B, s_q, H, 512], dtype o_lat_dtype (MLA_FP32 or MLA_BF16)
@@ -156,15 +160,20 @@ mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
  * mla_decode_partial followed by mla_decode_combine on the same workspace.
  *
  * mla_decode_partial: same arguments as mla_decode_attn minus the outputs.
- *   Scans split s of every sequence and writes into the workspace, with
- *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits) and
- *   R = s_q * H:
- *     part_o   fp32 [B, S, R, 512] at workspace offset 0: the normalised partial
- *              latent output of split s for each of the R query rows;
- *     part_lse fp32 [B, S, R] at byte offset align256(B * S * 512 * R * 4): the
- *              base-2 log-sum-exp of split s's scaled scores (-inf when the
- *              split holds no visible row).
- * mla_decode_combine: merges the S partials of every query row with weights
+ *   Scans every part and writes into the workspace, with
+ *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits),
+ *   R = s_q * H and M = B * (S + 1) partial slots (aligned = rounded up to a
+ *   multiple of 256 bytes):
+ *     part_o    fp32 [M, R, 512] at offset 0: slot m holds the normalised
+ *               partial latent output of one part for each of the R rows;
+ *     part_lse  fp32 [M, R] at aligned(M * R * 512 * 4): the base-2
+ *               log-sum-exp of the part's scaled scores (-inf when it holds
+ *               no visible row);
+ *     seg_first int32 [B], then seg_count int32 [B], at aligned(...) after
+ *               part_lse: sequence b's parts are the slots seg_first[b] ..
+ *               seg_first[b] + seg_count[b] - 1, in row order.
+ *   Slots outside every sequence's run are left unwritten.
+ * mla_decode_combine: merges the parts of every query row with weights
  *   2^(lse_s - max_s lse_s) and writes o_lat and (if not NULL) the natural-log
  *   lse, exactly as mla_decode_attn does.  B, s_q, H, max_seqlen and
  *   num_splits must be those given to mla_decode_partial. */

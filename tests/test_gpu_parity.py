@@ -130,9 +130,11 @@ def test_split_count_invariance_and_determinism(mla, kind):
     for ns in (1, 2, 3, 0):
         _, o_lat, lse, out = _run_steps(mla, inp, num_splits=ns)
         results[ns] = (_f64(o_lat), _f64(out))
+    # different split plans round the bf16 probabilities against different
+    # softmax references: allow one bf16 unit of the value on top of 2e-3
     base = results[1][0]
     for ns, (o, _) in results.items():
-        assert np.max(np.abs(o - base)) < 2e-3, ns
+        assert np.max(np.abs(o - base) - 2.0 ** -8 * np.abs(base)) < 2e-3, ns
     # fixed split plan: bitwise identical run to run
     _, o2, _, out2 = _run_steps(mla, inp, num_splits=0)
     np.testing.assert_array_equal(_f64(o2), results[0][0])
@@ -239,3 +241,24 @@ def test_full_size_sampled(mla, name):
         sel[b, :, h] = True
     m = _assert_close(got[sel], ref[sel], fp8=w.cache_dtype == "fp8", what=name)
     print(f"[parity-full] {name}: {m}", flush=True)
+
+
+# ----------------------------------------------------------------------------
+# the balanced work plan over ragged lengths
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["many_short", "very_ragged", "very_ragged_paged"])
+@pytest.mark.parametrize("ns", [0, 1, 3])
+def test_ragged_work_plan(mla, case, ns):
+    """Sequences of very different lengths share the equal tile ranges: each
+    tile is scanned exactly once and each sequence's parts merge to the
+    oracle, for more sequences than scan chunks and for forced split counts."""
+    w = dict(
+        many_short=W.Workload("many_short", B=300, H=16, s_q=1, causal=False, T_range=(1, 300), seed=71),
+        very_ragged=W.Workload("very_ragged", B=7, H=128, s_q=2, causal=True, T_range=(2, 2000), seed=72),
+        very_ragged_paged=W.Workload("very_ragged_paged", B=7, H=64, s_q=1, causal=False, T_range=(1, 2000),
+                                     paged=True, seed=73),
+    )[case]
+    print(f"[parity] plan {case} ns={ns} lengths={W.generate(w)['seqlens'][:8]}", flush=True)
+    inp = W.generate(w)
+    *_, out = _run_steps(mla, inp, num_splits=ns)
+    _assert_close(_f64(out), O.naive_decode(inp, SCALE), what=f"{case} ns={ns}")
