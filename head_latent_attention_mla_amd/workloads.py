@@ -56,6 +56,7 @@ class Workload:
     scaling: str = "unit"                      # "unit" | "literal"
     seed: int = 0
     T_stride: Optional[int] = None             # contiguous row stride (>= T); pad rows NaN
+    topk: Optional[int] = None                 # sparse decode: rows selected per sequence
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -82,6 +83,9 @@ WORKLOADS = {
     # FP8-E4M3 latent cache with one fp32 scale per row, 2 query tokens.
     "fp8_cache": Workload("fp8_cache", B=64, H=128, s_q=2, causal=True, T=16384,
                           cache_dtype="fp8", seed=5),
+    # Sparse top-k decode: 2048 of 16384 cached rows selected per sequence.
+    "sparse_topk": Workload("sparse_topk", B=64, H=128, s_q=1, causal=False, T=16384,
+                            topk=2048, seed=6),
 }
 
 
@@ -233,6 +237,25 @@ def generate(w: Workload, seed: Optional[int] = None, fill_pad: bool = True) -> 
     out.update(rows=pool, row_scale=pscale, block_table=block_table,
                block_size=BLOCK, max_blocks=max_blocks)
     return out
+
+
+def generate_selection(inp: dict, k: Optional[int] = None, seed: Optional[int] = None):
+    """A sparse selection for sparse decode: per sequence, min(k, T_b) distinct
+    cached positions drawn uniformly without replacement, in increasing order.
+    Returns (sel_idx int32 [B, k_max] padded with -1, sel_count int32 [B]).
+    Drawn from ``seed`` (default: the workload seed + 1000), after and apart
+    from the other inputs."""
+    w = inp["workload"]
+    k = w.topk if k is None else k
+    rng = np.random.default_rng(w.seed + 1000 if seed is None else seed)
+    seqlens = inp["seqlens"]
+    B = len(seqlens)
+    counts = np.minimum(k, seqlens).astype(np.int32)
+    k_max = int(counts.max())
+    sel = np.full((B, k_max), -1, dtype=np.int32)
+    for b in range(B):
+        sel[b, : counts[b]] = np.sort(rng.choice(int(seqlens[b]), size=int(counts[b]), replace=False))
+    return sel, counts
 
 
 def as_contiguous(inp: dict) -> dict:

@@ -6,5 +6,5 @@ never does, and shares no code with it.
 """
 from .mla_oracle import (  # noqa: F401
     absorb_out, absorb_q, absorbed_decode, bf16_to_f64, compare, e4m3_to_f64,
-    latent_attention, naive_decode, sequence_rows, visible_rows,
+    latent_attention, naive_decode, sequence_rows, sparse_decode, visible_rows,
 )

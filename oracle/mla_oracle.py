@@ -166,6 +166,44 @@ def naive_decode(inp: dict, scale: float, causal: Optional[bool] = None,
 
 
 # ----------------------------------------------------------------------------
+# sparse top-k decode: attention over a selected subset of the cached rows
+# ----------------------------------------------------------------------------
+def sparse_decode(inp: dict, sel_idx: np.ndarray, sel_count: np.ndarray, scale: float,
+                  pairs: Optional[Iterable[Tuple[int, int]]] = None) -> np.ndarray:
+    """out[b, j, h, :] attending only over the selected cached rows of sequence b.
+
+    "Why MLA and MTP Fight Each Other", section 6: a selector keeps the top-k
+    cached latents and attention runs over those alone, gathered by index
+    (the cost goes from the context length to k).  Here the selection of
+    sequence b is the positions sel_idx[b, :sel_count[b]] of its cache, shared
+    by its s_q query tokens, and it is the whole visible set (no further
+    mask).  The arithmetic is the expand form of ``naive_decode`` applied to
+    the gathered rows, in the listed order (repeats count once each).
+    """
+    q = bf16_to_f64(inp["q"])
+    w_uk = bf16_to_f64(inp["w_uk"])
+    w_uv = bf16_to_f64(inp["w_uv"])
+    B, s_q, H, _ = q.shape
+    out = np.full((B, s_q, H, D_V), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(H)]
+    by_b = {}
+    for b, h in pairs:
+        by_b.setdefault(b, []).append(h)
+    for b, heads in by_b.items():
+        n = int(sel_count[b])
+        C = sequence_rows(inp, b)[np.asarray(sel_idx[b, :n], dtype=np.int64)]
+        lat, rope = C[:, :D_C], C[:, D_C:]
+        for h in heads:
+            keys = np.concatenate([lat @ w_uk[h].T, rope], axis=1)
+            vals = lat @ w_uv[h]
+            for j in range(s_q):
+                p, _ = _softmax_weights((keys @ q[b, j, h]) * scale)
+                out[b, j, h] = p @ vals
+    return out
+
+
+# ----------------------------------------------------------------------------
 # the three absorbed steps, each alone
 # ----------------------------------------------------------------------------
 def absorb_q(q: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
