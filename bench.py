@@ -103,7 +103,7 @@ def copy_calibration(steps: int):
                       "us_per_launch": round(us, 2), "copy_gbs": round(2 * COPY_BYTES / us / 1e3, 1)}), flush=True)
 
 
-def cpu_baseline(inp, scale, seconds_target=15.0):
+def cpu_baseline(inp, scale, seconds_target=15.0, selection=None):
     """The fp64 oracle (naive expand-then-attend) on a bounded sample of (b, h)
     pairs of the same workload, scaled to the step's metric: the absorbed-path
     FLOPs of the sampled pairs (the same counting rule as the GPU figure) per
@@ -117,10 +117,13 @@ def cpu_baseline(inp, scale, seconds_target=15.0):
     flops, done, t0 = 0, 0, time.perf_counter()
     while time.perf_counter() - t0 < seconds_target:
         pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
-        oracle.naive_decode(inp, scale, pairs=pairs)
+        if selection is None:
+            oracle.naive_decode(inp, scale, pairs=pairs)
+        else:
+            oracle.sparse_decode(inp, selection[0], selection[1], scale, pairs=pairs)
         for b, _ in pairs:
-            T = int(inp["seqlens"][b])
-            vis = sum((T - w.s_q + j + 1) if w.causal else T for j in range(w.s_q))
+            T = int(inp["seqlens"][b]) if selection is None else int(selection[1][b])
+            vis = sum((T - w.s_q + j + 1) if (w.causal and selection is None) else T for j in range(w.s_q))
             flops += vis * (2 * 576 + 2 * 512) + 2 * 2 * 128 * 512 * w.s_q
         done += len(pairs)
     dt = time.perf_counter() - t0
@@ -131,7 +134,8 @@ def cpu_baseline(inp, scale, seconds_target=15.0):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done} random (sequence, head) pairs of the {w.name} workload (B={w.B} H={w.H} "
-                  f"s_q={w.s_q} T={w.T or w.T_range}), fp64 numpy naive expand-then-attend, {dt:.1f} s; "
+                  f"s_q={w.s_q} T={w.T or w.T_range}{'' if selection is None else f' top-{w.topk}'}), "
+                  f"fp64 numpy {'naive' if selection is None else 'sparse'} expand-then-attend, {dt:.1f} s; "
                   f"value = absorbed-path FLOPs of those pairs per second",
         "tokens_per_s": done / w.H * w.s_q / dt,
     }
@@ -181,9 +185,19 @@ def main():
                                       block_table=cache0.block_table))
     B, s_q, H = w.B, w.s_q, w.H
     N = B * s_q
+    sparse = w.topk is not None
+    selection = W.generate_selection(inp) if sparse else None
     q_lat = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=dev)
     out = torch.empty((B, s_q, H, 128), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(mla.decode_workspace_bytes(B, s_q, H, cache0.max_seqlen), dtype=torch.uint8, device=dev)
+    if sparse:
+        sel_idx = torch.from_numpy(selection[0]).to(dev)
+        sel_count = torch.from_numpy(selection[1]).to(dev)
+        scan_len = int(sel_idx.shape[1])
+        ws = torch.empty(mla.sparse_workspace_bytes(B, s_q, H, scan_len, fp8=cache0.fp8), dtype=torch.uint8,
+                         device=dev)
+    else:
+        scan_len = cache0.max_seqlen
+        ws = torch.empty(mla.decode_workspace_bytes(B, s_q, H, scan_len), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -193,10 +207,13 @@ def main():
         mla.absorb_q(q.view(N, H, -1), w_uk, out=q_lat.view(N, H, -1))
         if ev is not None:
             ev[1].record(stream)
-        mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws)
+        if sparse:
+            mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws)
+        else:
+            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
-        mla.decode_combine_out(ws, w_uv, B, s_q, H, c.max_seqlen, out=out.view(N, H, -1))
+        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1))
         if ev is not None:
             ev[3].record(stream)
 
@@ -217,7 +234,7 @@ def main():
 
     # per-kernel durations with HIP events on the launch stream (recorded
     # back to back, read after one synchronisation)
-    names = ["absorb_q", "decode_split", "combine_out"]
+    names = ["absorb_q", "sparse_gather+decode_split" if sparse else "decode_split", "combine_out"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -230,27 +247,29 @@ def main():
     kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
 
     fp8 = w.cache_dtype == "fp8"
-    cnt = algorithmic_counts(B, s_q, H, [int(x) for x in inp["seqlens"]], w.causal,
+    rows_read = [int(x) for x in (selection[1] if sparse else inp["seqlens"])]
+    cnt = algorithmic_counts(B, s_q, H, rows_read, w.causal and not sparse,
                              cache_elem_bytes=1 if fp8 else 2, scale_bytes=4 if fp8 else 0)
     s = ms_per_step * 1e-3
     tflops = cnt["flops_step"] / s / 1e12
-    split_s = kern_us["decode_split"] * 1e-6
+    split_s = kern_us[names[1]] * 1e-6
     scan_gbs = cnt["bytes_scan"] / split_s / 1e9
     scan_tflops = cnt["flops_scan"] / split_s / 1e12
     # the path at s_q = 1 with a bf16 cache sits below the bf16 ridge (HBM-bound);
     # more query tokens per cached row or an fp8 cache push it past (MFMA-bound)
     hbm_bound = (not fp8) and s_q == 1
     roofline = {
-        "kernel": "decode_split (split-T latent scan)",
+        "kernel": ("sparse gather + split-T scan (selected rows counted once)" if sparse
+                   else "decode_split (split-T latent scan)"),
         "bound": "hbm" if hbm_bound else "mfma",
         "achieved": round(scan_gbs if hbm_bound else scan_tflops, 1),
         "peak": HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS,
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
         "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / BF16_PEAK_TFLOPS), 4),
-        "traffic": measured_traffic(w.name),
+        "traffic": None if sparse else measured_traffic(w.name),
         "algorithmic_bytes_per_launch": cnt["bytes_scan"],
         "algorithmic_flops_per_launch": cnt["flops_scan"],
-        "avg_launch_us": round(kern_us["decode_split"], 2),
+        "avg_launch_us": round(kern_us[names[1]], 2),
         "achieved_tflops": round(scan_tflops, 1),
         "achieved_gbs": round(scan_gbs, 1),
     }
@@ -267,7 +286,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={B} H={H} s_q={s_q} T={w.T or w.T_range} "
+        "config": {"workload": f"{w.name}: B={B} H={H} s_q={s_q} T={w.T or w.T_range}"
+                               f"{f' top-{w.topk} selected' if sparse else ''} "
                                f"{'paged' if w.paged else 'contiguous'} {w.cache_dtype} latent cache [*, 576], "
                                f"{'causal' if w.causal else 'non-causal'}, seed {w.seed}",
                    "global_batch": B, "seq_len": w.max_T, "parallelism": "single GPU"},
@@ -276,7 +296,7 @@ def main():
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "roofline": roofline,
     }
-    if args.naive_steps > 0:
+    if args.naive_steps > 0 and not sparse:
         # the ablation: same inputs and output, every cached row expanded per head
         nws = torch.empty(mla.naive_workspace_bytes(B, s_q, H, cache0.max_seqlen), dtype=torch.uint8, device=dev)
         out_n = torch.empty_like(out)
@@ -299,7 +319,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(inp, scale, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(inp, scale, args.cpu_seconds, selection)
     print(json.dumps(rec), flush=True)
 
 

@@ -227,6 +227,92 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
                                            (uint16_t*)out, N, H, (hipStream_t)stream));
 }
 
+namespace {
+
+// Sparse workspace: [scan workspace for max_seqlen = k_max][compact rows]
+// [clamped counts][compact scales (e4m3 only)]
+bool sparse_layout(int32_t B, int32_t s_q, int32_t H, int32_t k_max, int32_t num_splits, int32_t dtype,
+                   Plan* pl, size_t* rows_off, size_t* count_off, size_t* scale_off, size_t* total) {
+  if (k_max <= 0 || (dtype != MLA_BF16 && dtype != MLA_FP8_E4M3)) return false;
+  if (!make_plan(B, s_q, H, k_max, num_splits, pl)) return false;
+  const size_t eb = dtype == MLA_FP8_E4M3 ? 1 : 2;
+  *rows_off = pl->ws_bytes;
+  *count_off = *rows_off + align_up((size_t)B * k_max * mla::ROWW * eb);
+  *scale_off = *count_off + align_up((size_t)B * sizeof(int32_t));
+  *total = *scale_off + (dtype == MLA_FP8_E4M3 ? align_up((size_t)B * k_max * sizeof(float)) : 0);
+  return true;
+}
+
+}  // namespace
+
+size_t mla_sparse_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t k_max, int32_t num_splits,
+                                  int32_t cache_dtype) {
+  Plan pl;
+  size_t ro, co, so, total;
+  if (!sparse_layout(B, s_q, H, k_max, num_splits, cache_dtype, &pl, &ro, &co, &so, &total)) return 0;
+  return total;
+}
+
+mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv, const int32_t* sel_idx,
+                                     const int32_t* sel_count, int32_t k_max, int32_t B, int32_t s_q,
+                                     int32_t H, float softmax_scale, void* workspace, size_t ws_bytes,
+                                     int32_t num_splits, void* stream) {
+  if (q_lat == nullptr || sel_idx == nullptr || sel_count == nullptr) return MLA_ERR_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || k_max <= 0 || num_splits < 0) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, 1);
+  if (ks != MLA_OK) return ks;
+  Plan pl;
+  size_t rows_off, count_off, scale_off, total;
+  if (!sparse_layout(B, s_q, H, k_max, num_splits, kv->dtype, &pl, &rows_off, &count_off, &scale_off, &total))
+    return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < total) return MLA_ERR_WORKSPACE;
+  const bool fp8 = kv->dtype == MLA_FP8_E4M3;
+  mla::GatherParams g{};
+  g.rows = kv->rows;
+  g.row_scale = kv->row_scale;
+  g.block_table = kv->block_table;
+  g.seqlens = kv->seqlens;
+  g.sel_idx = sel_idx;
+  g.sel_count = sel_count;
+  g.out_rows = (char*)workspace + rows_off;
+  g.out_scale = fp8 ? (float*)((char*)workspace + scale_off) : nullptr;
+  g.out_count = (int32_t*)((char*)workspace + count_off);
+  g.T_stride = kv->T_stride;
+  g.max_blocks = kv->max_blocks;
+  g.B = B;
+  g.k_max = k_max;
+  g.fp8 = fp8;
+  const hipError_t e = mla::launch_gather(g, (hipStream_t)stream);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  // scan the compact cache: sequence b holds sel_count[b] rows, no causal mask
+  mla_kv_desc compact{};
+  compact.rows = g.out_rows;
+  compact.row_scale = g.out_scale;
+  compact.block_table = nullptr;
+  compact.seqlens = g.out_count;
+  compact.dtype = kv->dtype;
+  compact.T_stride = k_max;
+  compact.block_size = 0;
+  compact.max_blocks = 0;
+  compact.max_seqlen = k_max;
+  return decode_partial_impl(q_lat, &compact, B, s_q, H, softmax_scale, 0, workspace, pl.ws_bytes, num_splits,
+                             (hipStream_t)stream);
+}
+
+mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv, const int32_t* sel_idx,
+                                  const int32_t* sel_count, int32_t k_max, int32_t B, int32_t s_q, int32_t H,
+                                  float softmax_scale, void* o_lat, int32_t o_lat_dtype, float* lse,
+                                  void* workspace, size_t ws_bytes, int32_t num_splits, void* stream) {
+  if (o_lat == nullptr) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  const mla_status s = mla_sparse_decode_partial(q_lat, kv, sel_idx, sel_count, k_max, B, s_q, H, softmax_scale,
+                                                 workspace, ws_bytes, num_splits, stream);
+  if (s != MLA_OK) return s;
+  return decode_combine_impl(B, s_q, H, k_max, num_splits, workspace, ws_bytes, o_lat, o_lat_dtype, lse,
+                             (hipStream_t)stream);
+}
+
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
   if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || H > (1 << 16)) return 0;
   // W_UV re-laid out per head with the latent dimension contiguous

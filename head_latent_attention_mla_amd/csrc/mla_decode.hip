@@ -191,8 +191,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     for (int bb = c0; bb < c1; ++bb) tiles_mine += (p.seqlens[bb] + KT - 1) / KT;
     (void)inclusive_scan(tiles_mine);
     const int64_t total = uniform64(found[2]);
-    auto parts_of = [&](int bb) -> int {     // in [1, n_t]: every part holds a tile
+    // in [1, max(n_t, 1)]: every part holds a tile, and a sequence without
+    // rows still gets one (empty) part, whose partial merges to zero
+    auto parts_of = [&](int bb) -> int {
       const int64_t nt = (p.seqlens[bb] + KT - 1) / KT;
+      if (total == 0 || nt == 0) return 1;
       const int64_t q = floor_div(nt * p.n_ranges, total);
       return (int)(q < 1 ? 1 : (q > nt ? nt : q));
     };

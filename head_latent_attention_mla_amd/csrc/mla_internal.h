@@ -59,7 +59,25 @@ struct NaiveParams {
 };
 constexpr int NAIVE_MAX_SQ = 4;
 
+// One gather of selected cache rows into a compact contiguous cache.
+struct GatherParams {
+  const void* rows;             // source cache rows (contiguous or pool), bf16 or e4m3
+  const float* row_scale;       // e4m3 only
+  const int32_t* block_table;   // paged source only (else null)
+  const int32_t* seqlens;       // [B] source lengths
+  const int32_t* sel_idx;       // [B, k_max] selected positions
+  const int32_t* sel_count;     // [B] entries used per sequence
+  void* out_rows;               // [B, k_max, 576] compact rows
+  float* out_scale;             // [B, k_max] (e4m3 only)
+  int32_t* out_count;           // [B] counts clamped to [0, k_max]
+  int64_t T_stride;
+  int32_t max_blocks;
+  int32_t B, k_max;
+  int32_t fp8;
+};
+
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
                           const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,
                           hipStream_t stream);

@@ -61,6 +61,11 @@ SIGNATURES = {
     "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
     "mla_absorb_out": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
     "mla_decode_combine_out": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, _I32, _VP, _VP]),
+    "mla_sparse_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "mla_sparse_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _I32, _F32,
+                                         _VP, _SZ, _I32, _VP]),
+    "mla_sparse_decode_attn": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _I32, _F32,
+                                      _VP, _I32, _VP, _VP, _SZ, _I32, _VP]),
     "mla_naive_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_naive_decode": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP,
                                 _VP, _SZ, _VP]),
@@ -293,6 +298,66 @@ def decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.
         return out.view(B, s_q, H, D_V)
     o_lat, _ = decode_attn(q_lat, cache, scale, causal, o_dtype, num_splits, want_lse=False, stream=stream)
     return absorb_out(o_lat.view(B * s_q, H, D_C), w_uv, stream=stream).view(B, s_q, H, D_V)
+
+
+def sparse_workspace_bytes(B: int, s_q: int, H: int, k_max: int, num_splits: int = 0, fp8: bool = False) -> int:
+    return int(_lib.mla_sparse_workspace_bytes(B, s_q, H, k_max, num_splits, MLA_FP8_E4M3 if fp8 else MLA_BF16))
+
+
+def _sparse_args(q_lat, cache, sel_idx, sel_count):
+    B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
+    if sel_idx.dim() != 2 or sel_idx.shape[0] != B:
+        raise ValueError("sel_idx must be [B, k_max]")
+    _require(sel_idx, "sel_idx", torch.int32, tuple(sel_idx.shape))
+    _require(sel_count, "sel_count", torch.int32, (B,))
+    return B, s_q, H, int(sel_idx.shape[1])
+
+
+def sparse_decode_partial(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torch.Tensor, sel_count: torch.Tensor,
+                          scale: float = DEFAULT_SCALE, num_splits: int = 0,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Sparse top-k scan into a workspace (returned): attention over the rows
+    sel_idx[b, :sel_count[b]] of each sequence.  Merge with decode_combine /
+    decode_combine_out using k_max = sel_idx.shape[1] as max_seqlen."""
+    B, s_q, H, k_max = _sparse_args(q_lat, cache, sel_idx, sel_count)
+    kv = cache.desc()
+    need = sparse_workspace_bytes(B, s_q, H, k_max, num_splits, cache.fp8)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    _check(_lib.mla_sparse_decode_partial(_ptr(q_lat), ctypes.byref(kv), _ptr(sel_idx), _ptr(sel_count), k_max,
+                                          B, s_q, H, float(scale), _ptr(workspace), workspace.numel(), num_splits,
+                                          _stream(stream)), "mla_sparse_decode_partial")
+    return workspace
+
+
+def sparse_decode_attn(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torch.Tensor, sel_count: torch.Tensor,
+                       scale: float = DEFAULT_SCALE, o_dtype=torch.float32, num_splits: int = 0,
+                       want_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Sparse top-k latent attention: returns (o_lat [B, s_q, H, 512], lse [B, s_q, H] or None)."""
+    B, s_q, H, k_max = _sparse_args(q_lat, cache, sel_idx, sel_count)
+    kv = cache.desc()
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
+    o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=q_lat.device)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device) if want_lse else None
+    need = sparse_workspace_bytes(B, s_q, H, k_max, num_splits, cache.fp8)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+    _check(_lib.mla_sparse_decode_attn(_ptr(q_lat), ctypes.byref(kv), _ptr(sel_idx), _ptr(sel_count), k_max,
+                                       B, s_q, H, float(scale), _ptr(o_lat), dt, _ptr(lse), _ptr(workspace),
+                                       workspace.numel(), num_splits, _stream(stream)), "mla_sparse_decode_attn")
+    return o_lat, lse
+
+
+def sparse_decode(q: torch.Tensor, cache: LatentCache, sel_idx: torch.Tensor, sel_count: torch.Tensor,
+                  w_uk: torch.Tensor, w_uv: torch.Tensor, scale: float = DEFAULT_SCALE, num_splits: int = 0,
+                  stream=None) -> torch.Tensor:
+    """Sparse absorbed decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16."""
+    B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
+    q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
+    ws = sparse_decode_partial(q_lat, cache, sel_idx, sel_count, scale, num_splits, stream=stream)
+    out = decode_combine_out(ws, w_uv, B, s_q, H, int(sel_idx.shape[1]), num_splits, stream=stream)
+    return out.view(B, s_q, H, D_V)
 
 
 def naive_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int) -> int:

@@ -219,6 +219,42 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
                                   const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
                                   float* lse, void* stream);
 
+/* Sparse top-k decode ("Why MLA and MTP Fight Each Other", section 6: a
+ * selector keeps the top-k cached latents and attention runs over those only,
+ * gathered by index; the cost follows k instead of the context length).
+ * The selection of sequence b is sel_idx[b, 0 .. sel_count[b] - 1]:
+ * positions in its cache (0 <= pos < seqlens[b]), in any order; a repeated
+ * position counts once per entry; a position outside that range gathers a
+ * zero row (nothing is read for it).  The selection is the visible set of all
+ * s_q query tokens of the sequence (no causal mask); a sequence with no
+ * selected row gets zeros.  For query token j, head h:
+ *   o_lat[b,j,h,:] = sum_{i < sel_count[b]} softmax_i(scale * <q_lat[b,j,h,:],
+ *                    row_{sel_idx[b,i]}>) * row_{sel_idx[b,i]}[0:512]
+ * Steps: the selected rows are gathered into a compact cache inside the
+ * workspace, which the split-T scan of mla_decode_partial reads.
+ *   kv         the full cache (contiguous or paged, bf16 or e4m3)
+ *   sel_idx    int32 [B, k_max]; sel_count int32 [B], each <= k_max
+ *   k_max      row stride of sel_idx and the largest selection (>= s_q)
+ *   workspace  ws_bytes >= mla_sparse_workspace_bytes(B, s_q, H, k_max,
+ *              num_splits, kv->dtype).  Its first part has the layout of
+ *              mla_decode_partial's workspace with max_seqlen = k_max, so
+ *              mla_decode_combine and mla_decode_combine_out (given k_max as
+ *              max_seqlen) merge the partials of mla_sparse_decode_partial.
+ * mla_sparse_decode_attn = mla_sparse_decode_partial + mla_decode_combine. */
+size_t mla_sparse_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t k_max,
+                                  int32_t num_splits, int32_t cache_dtype);
+mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv,
+                                     const int32_t* sel_idx, const int32_t* sel_count,
+                                     int32_t k_max, int32_t B, int32_t s_q, int32_t H,
+                                     float softmax_scale, void* workspace, size_t ws_bytes,
+                                     int32_t num_splits, void* stream);
+mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv,
+                                  const int32_t* sel_idx, const int32_t* sel_count,
+                                  int32_t k_max, int32_t B, int32_t s_q, int32_t H,
+                                  float softmax_scale, void* o_lat, int32_t o_lat_dtype,
+                                  float* lse, void* workspace, size_t ws_bytes,
+                                  int32_t num_splits, void* stream);
+
 /* Ablation only -- the naive up-project-then-attend form ("The MLA decode
  * speedup hiding in your model card", "The naive form, written out"; "Why MLA
  * and MTP Fight Each Other", section 5.1, expand bracketing).  Every visible

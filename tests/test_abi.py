@@ -154,3 +154,22 @@ def test_combine_out_rejects_bad_arguments(m):
     assert co(0, 1, 16, 256, 0, 0x1000, need, 0x3000, 0x2000, None, 2, None, None) == ARG
     assert co(2, 1, 16, 256, 0, 0x1000, need - 1, 0x3000, 0x2000, None, 2, None, None) == WS
     assert co(2, 1, 16, 256, 0, None, need, 0x3000, 0x2000, None, 2, None, None) == WS
+
+
+def test_sparse_rejects_bad_arguments(m):
+    wsb = m._lib.mla_sparse_workspace_bytes
+    base = m._lib.mla_decode_workspace_bytes(2, 1, 16, 64, 0)
+    assert wsb(2, 1, 16, 64, 0, 0) == base + 2 * 64 * 576 * 2 + 256             # + compact bf16 rows + counts
+    assert wsb(2, 1, 16, 64, 0, 1) == base + 2 * 64 * 576 + 256 + 512           # + e4m3 rows + counts + scales
+    assert wsb(2, 1, 16, 0, 0, 0) == 0 and wsb(2, 1, 16, 64, 0, 2) == 0
+    sp = m._lib.mla_sparse_decode_partial
+    need = wsb(2, 1, 16, 64, 0, 0)
+    assert sp(0x3000, ctypes.byref(_kv()), None, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, None, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 0, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.0, 0x5000, need, 0, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv(rows=None)), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need - 1, 0, None) == WS
+    sa = m._lib.mla_sparse_decode_attn
+    assert sa(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, None, 2, None, 0x5000, need, 0,
+              None) == ARG

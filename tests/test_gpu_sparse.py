@@ -1,0 +1,97 @@
+"""Sparse top-k decode through the C ABI against the fp64 oracle's sparse
+form ("Why MLA and MTP Fight Each Other", section 6).  Bars as for the dense
+path: max-abs <= 2e-2 beyond the final bf16 output rounding and relative L2
+<= 5e-3; FP8 caches max-abs <= 6e-2."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from head_latent_attention_mla_amd import workloads as W
+
+from test_gpu_parity import SCALE, _assert_close, _f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from head_latent_attention_mla_amd import mla as m
+    return m
+
+
+CASES = dict(
+    contig=(W.Workload("sp_contig", B=3, H=128, s_q=1, causal=False, T=700, seed=81), 130),
+    paged=(W.Workload("sp_paged", B=4, H=64, s_q=2, causal=False, T_range=(100, 900), paged=True, seed=82), 200),
+    fp8=(W.Workload("sp_fp8", B=2, H=128, s_q=1, causal=False, T=500, cache_dtype="fp8", seed=83), 257),
+    wide=(W.Workload("sp_wide", B=5, H=16, s_q=3, causal=False, T_range=(10, 300), seed=84), 64),
+)
+
+
+def _run(mla, inp, sel, cnt, num_splits=0):
+    q, w_uk, w_uv, cache = W.to_torch(inp)
+    s = torch.from_numpy(sel).cuda()
+    c = torch.from_numpy(cnt).cuda()
+    out = mla.sparse_decode(q, cache, s, c, w_uk, w_uv, SCALE, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kind", list(CASES))
+def test_sparse_vs_oracle(mla, kind):
+    w, k = CASES[kind]
+    inp = W.generate(w)
+    sel, cnt = W.generate_selection(inp, k=k)
+    print(f"[sparse] {kind} k={k} counts={cnt}", flush=True)
+    out = _run(mla, inp, sel, cnt)
+    m = _assert_close(_f64(out), O.sparse_decode(inp, sel, cnt, SCALE), fp8=w.cache_dtype == "fp8",
+                      what=f"sparse {kind}")
+    print(f"[sparse] {kind}: {m}", flush=True)
+
+
+def test_sparse_split_counts_and_order(mla):
+    w, k = CASES["contig"]
+    inp = W.generate(w)
+    sel, cnt = W.generate_selection(inp, k=k)
+    ref = O.sparse_decode(inp, sel, cnt, SCALE)
+    for ns in (1, 3):
+        _assert_close(_f64(_run(mla, inp, sel, cnt, num_splits=ns)), ref, what=f"ns={ns}")
+    rev = sel.copy()
+    for b in range(w.B):
+        rev[b, : cnt[b]] = rev[b, : cnt[b]][::-1]
+    _assert_close(_f64(_run(mla, inp, rev, cnt)), ref, what="reversed selection")
+
+
+def test_sparse_edge_selections(mla):
+    """A repeated position counts twice, an empty selection gives zeros, a
+    selection of every row in order equals the dense decode, and a count past
+    k_max is clamped to it."""
+    w = W.Workload("sp_edge", B=3, H=128, s_q=1, causal=False, T=150, seed=85)
+    inp = W.generate(w)
+    sel = np.full((3, 150), -1, dtype=np.int32)
+    sel[0, :5] = [3, 3, 40, 149, 0]
+    sel[2, :150] = np.arange(150)
+    cnt = np.array([5, 0, 150], dtype=np.int32)
+    out = _f64(_run(mla, inp, sel, cnt))
+    ref = O.sparse_decode(inp, sel, cnt, SCALE, pairs=[(0, h) for h in range(w.H)])
+    _assert_close(out[0], ref[0], what="repeat")
+    assert np.all(out[1] == 0.0)
+    _assert_close(out[2], O.naive_decode(inp, SCALE)[2], what="all rows")
+    cnt_big = np.array([5, 0, 1000], dtype=np.int32)
+    _assert_close(_f64(_run(mla, inp, sel, cnt_big))[2], O.naive_decode(inp, SCALE)[2], what="clamped count")
+
+
+def test_sparse_full_size_sampled(mla):
+    """2048 of 16384 rows per sequence, B=64, H=128; sampled (sequence, head)."""
+    w = W.WORKLOADS["sparse_topk"]
+    print(f"[sparse] full {w}", flush=True)
+    inp = W.generate(w)
+    sel, cnt = W.generate_selection(inp)
+    got = _f64(_run(mla, inp, sel, cnt))
+    rng = np.random.default_rng(5)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(6)] + [(0, 0), (w.B - 1, w.H - 1)]
+    ref = O.sparse_decode(inp, sel, cnt, SCALE, pairs=pairs)
+    for b, h in pairs:
+        _assert_close(got[b, :, h], ref[b, :, h], what=f"sparse full ({b},{h})")
