@@ -141,6 +141,119 @@ def cpu_baseline(inp, scale, seconds_target=15.0, selection=None):
     }
 
 
+def append_main(args, w):
+    """The latent append step alone: N tokens projected through the
+    [576, d_model] weight, rotated and stored into the cache.  HBM-bound on
+    the weight; the weight rotates over enough copies that the 256 MB
+    last-level cache cannot hold them."""
+    import torch
+    from head_latent_attention_mla_amd import workloads as W
+    from head_latent_attention_mla_amd import mla
+
+    print(f"[bench] generating {w}", file=sys.stderr, flush=True)
+    inp = W.generate_append(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8 = w.cache_dtype == "fp8"
+
+    def bf16(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    x = bf16(inp["x"])
+    w_bytes = 576 * w.d_model * 2
+    n_w = max(2, -(-320 * 2 ** 20 // w_bytes))
+    weights = [bf16(inp["w_dkr"])]
+    weights += [weights[0].clone() for _ in range(n_w - 1)]
+    seq_id = torch.from_numpy(inp["seq_id"]).to(dev)
+    pos = torch.from_numpy(inp["pos"]).to(dev)
+    n_rows = w.B * w.T_cap
+    if w.paged:
+        rows = torch.zeros((n_rows // 64, 64, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        table = torch.arange(n_rows // 64, dtype=torch.int32, device=dev).view(w.B, w.T_cap // 64)
+    else:
+        rows = torch.zeros((w.B, w.T_cap, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        table = None
+    scale_t = torch.zeros(rows.shape[:2], dtype=torch.float32, device=dev) if fp8 else None
+    cache = mla.LatentCache(rows=rows, seqlens=torch.full((w.B,), w.T_cap, dtype=torch.int32, device=dev),
+                            max_seqlen=w.T_cap, row_scale=scale_t, block_table=table)
+    ws = torch.empty(mla.append_workspace_bytes(w.N, w.d_model), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        mla.latent_append(x, weights[i % n_w], seq_id, pos, cache, 10000.0, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # a call is a few microseconds of GPU work, less than the Python call
+    # takes: the timed calls (one per weight copy) are captured once in a HIP
+    # graph and replayed, so the GPU, not the host, sets the pace
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n_w):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-args.steps // n_w))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    n_calls = reps * n_w
+    ms = t0.elapsed_time(t1) / n_calls
+    s = ms * 1e-3
+    row_bytes = 576 * (1 if fp8 else 2) + (4 if fp8 else 0)
+    alg_bytes = w_bytes + w.N * w.d_model * 2 + w.N * row_bytes + 8 * w.N
+    flops = 2 * w.N * w.d_model * 576
+    gbs = alg_bytes / s / 1e9
+    rec = {
+        "metric": "latent append HBM GB/s (% roofline)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_calls,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={w.N} tokens, d_model={w.d_model}, W_DKV|W_KR [576, {w.d_model}] bf16, "
+                               f"{'paged' if w.paged else 'contiguous'} {w.cache_dtype} cache of {w.B} x {w.T_cap} "
+                               f"slots, seed {w.seed}",
+                   "global_batch": w.N, "seq_len": w.T_cap, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.N / s, 1),
+        "roofline": {
+            "kernel": "latent append (append_project_kernel + append_finalize_kernel, one call)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes, "algorithmic_flops_per_launch": flops,
+            "avg_launch_us": round(ms * 1e3, 2), "achieved_tflops": round(flops / s / 1e12, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        from threadpoolctl import threadpool_info
+        from oracle import latent_append as oracle_append
+        from oracle import mla_oracle as oracle
+        xs = oracle.bf16_to_f64(inp["x"])
+        wd = oracle.bf16_to_f64(inp["w_dkr"])
+        done, t_start = 0, time.perf_counter()
+        while time.perf_counter() - t_start < min(args.cpu_seconds, 10.0) or done == 0:
+            oracle_append.append_rows(xs, wd, inp["pos"], 10000.0)
+            done += 1
+        dt = time.perf_counter() - t_start
+        rec["cpu_baseline"] = {
+            "value": round(done * alg_bytes / dt / 1e9, 3), "unit": "GB/s",
+            "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1]), "kind": "oracle",
+            "sample": f"{done} full calls of the fp64 numpy latent-append oracle on the same {w.N} tokens, {dt:.1f} s",
+        }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +284,9 @@ def main():
     from head_latent_attention_mla_amd import workloads as W
     from head_latent_attention_mla_amd import mla
 
+    if args.workload in W.APPEND_WORKLOADS:
+        append_main(args, W.APPEND_WORKLOADS[args.workload])
+        return
     w = W.WORKLOADS[args.workload]
     scale = 1.0 / math.sqrt(192.0)
     print(f"[bench] generating {w}", file=sys.stderr, flush=True)

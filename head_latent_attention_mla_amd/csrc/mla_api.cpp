@@ -74,6 +74,23 @@ mla_status check_kv(const mla_kv_desc* kv, int32_t s_q) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Split-K layout of the append projection: about kTargetWorkGroups
+// work-groups over the 18 column blocks and the 64-token blocks.
+constexpr int kAppendColBlocks = mla::ROWW / 32;
+bool append_split(int32_t N, int32_t d_model, int32_t* ks_count, int32_t* chunks_per_split) {
+  if (N <= 0 || N > (1 << 20) || d_model < 64 || d_model % 64 != 0 || d_model > (1 << 20)) return false;
+  const int64_t chunks = d_model / 64;
+  const int64_t nz = (N + 63) / 64;
+  int64_t ks = (kTargetWorkGroups + kAppendColBlocks * nz - 1) / (kAppendColBlocks * nz);
+  if (ks > chunks) ks = chunks;
+  if (ks < (chunks + 7) / 8) ks = (chunks + 7) / 8;     // at most 8 chunks (two per wave)
+  if (ks < 1) ks = 1;
+  const int64_t cps = (chunks + ks - 1) / ks;
+  *chunks_per_split = (int32_t)cps;
+  *ks_count = (int32_t)((chunks + cps - 1) / cps);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -352,4 +369,50 @@ mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv, const void* w_
   return hip_status(mla::launch_naive(p, (hipStream_t)stream));
 }
 
+size_t mla_append_workspace_bytes(int32_t N, int32_t d_model) {
+  int32_t ks, spp;
+  if (!append_split(N, d_model, &ks, &spp)) return 0;
+  return align_up((size_t)ks * N * mla::ROWW * sizeof(float));
+}
+
+mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_t d_model,
+                             const int32_t* seq_id, const int32_t* pos, float rope_base,
+                             const mla_kv_desc* kv, int32_t B, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  if (x == nullptr || w_dkr == nullptr || seq_id == nullptr || pos == nullptr || kv == nullptr) return MLA_ERR_ARG;
+  int32_t ks, spp;
+  if (!append_split(N, d_model, &ks, &spp)) return MLA_ERR_ARG;
+  if (B <= 0 || !std::isfinite(rope_base) || !(rope_base > 0.f)) return MLA_ERR_ARG;
+  if (kv->rows == nullptr) return MLA_ERR_ARG;
+  if (kv->dtype != MLA_BF16 && kv->dtype != MLA_FP8_E4M3) return MLA_ERR_ARG;
+  if ((kv->dtype == MLA_FP8_E4M3) != (kv->row_scale != nullptr)) return MLA_ERR_ARG;
+  if (kv->block_table != nullptr) {
+    if (kv->block_size != kTileRows) return MLA_ERR_UNSUPPORTED;
+    if (kv->max_blocks <= 0) return MLA_ERR_ARG;
+  } else if (kv->T_stride <= 0) {
+    return MLA_ERR_ARG;
+  }
+  if (workspace == nullptr || ws_bytes < mla_append_workspace_bytes(N, d_model)) return MLA_ERR_WORKSPACE;
+  mla::AppendParams p{};
+  p.x = (const uint16_t*)x;
+  p.w = (const uint16_t*)w_dkr;
+  p.part = (float*)workspace;
+  p.seq_id = seq_id;
+  p.pos = pos;
+  p.rows = const_cast<void*>(kv->rows);
+  p.row_scale = const_cast<float*>(kv->row_scale);
+  p.block_table = kv->block_table;
+  p.T_stride = kv->T_stride;
+  p.max_blocks = kv->max_blocks;
+  p.B = B;
+  p.N = N;
+  p.d = d_model;
+  p.ks_count = ks;
+  p.chunks_per_split = spp;
+  p.log2_base = std::log2((double)rope_base);
+  p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  return hip_status(mla::launch_append(p, (hipStream_t)stream));
+}
+
 }  // extern "C"
+

@@ -76,6 +76,25 @@ struct GatherParams {
   int32_t fp8;
 };
 
+// One latent append: project, rotate and store the rows of N new tokens.
+struct AppendParams {
+  const uint16_t* x;            // bf16 [N, d] hidden states
+  const uint16_t* w;            // bf16 [576, d]: W_DKV^T rows 0..511, W_KR^T rows 512..575
+  float* part;                  // workspace: fp32 [ks_count, N, 576] split-K partial rows
+  const int32_t* seq_id;        // [N] sequence of each token
+  const int32_t* pos;           // [N] position of each token in its sequence
+  void* rows;                   // cache rows (contiguous [B, T_stride] or pool), bf16 or e4m3
+  float* row_scale;             // e4m3 only
+  const int32_t* block_table;   // paged only (else null)
+  int64_t T_stride;
+  int32_t max_blocks;
+  int32_t B, N, d;
+  int32_t ks_count;             // K splits
+  int32_t chunks_per_split;     // 64-wide k-chunks per split
+  double log2_base;             // log2 of the rope base
+  int32_t fp8;
+};
+
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
@@ -89,5 +108,6 @@ hipError_t launch_combine_out(const float* part_o, const float* part_lse, const 
                               const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream);
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, hipStream_t stream);
 
 }  // namespace mla

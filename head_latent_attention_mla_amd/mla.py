@@ -69,6 +69,9 @@ SIGNATURES = {
     "mla_naive_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_naive_decode": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP,
                                 _VP, _SZ, _VP]),
+    "mla_append_workspace_bytes": (_SZ, [_I32, _I32]),
+    "mla_latent_append": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _F32, ctypes.POINTER(KVDesc), _I32, _VP, _SZ,
+                                 _VP]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
 }
 
@@ -382,3 +385,28 @@ def naive_decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: 
                                  int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "mla_naive_decode")
     return out
+
+
+def append_workspace_bytes(N: int, d_model: int) -> int:
+    return int(_lib.mla_append_workspace_bytes(N, d_model))
+
+
+def latent_append(x: torch.Tensor, w_dkr: torch.Tensor, seq_id: torch.Tensor, pos: torch.Tensor,
+                  cache: LatentCache, rope_base: float = 10000.0, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    """Write the cached rows of N new tokens: x [N, d] bf16 hidden states,
+    w_dkr [576, d] bf16 (W_DKV^T over W_KR^T); token n goes to position
+    pos[n] of sequence seq_id[n] of ``cache`` (its rows and scales are
+    written in place; its seqlens are not touched)."""
+    N, d = int(x.shape[0]), int(x.shape[1])
+    _require(x, "x", torch.bfloat16, (N, d))
+    _require(w_dkr, "w_dkr", torch.bfloat16, (ROW, d))
+    _require(seq_id, "seq_id", torch.int32, (N,))
+    _require(pos, "pos", torch.int32, (N,))
+    kv = cache.desc()
+    need = append_workspace_bytes(N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(_lib.mla_latent_append(_ptr(x), _ptr(w_dkr), N, d, _ptr(seq_id), _ptr(pos), float(rope_base),
+                                  ctypes.byref(kv), cache.B, _ptr(workspace), workspace.numel(),
+                                  _stream(stream)), "mla_latent_append")

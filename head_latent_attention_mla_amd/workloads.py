@@ -308,3 +308,52 @@ def to_torch(inp: dict, device="cuda"):
 def bf16_tensor_to_numpy_bits(t) -> np.ndarray:
     """bf16 device tensor -> numpy uint16 bit patterns."""
     return t.detach().contiguous().view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# latent append inputs
+# ----------------------------------------------------------------------------
+D_MODEL = 7168                  # DeepSeek-V3 hidden width
+
+
+@dataclasses.dataclass(frozen=True)
+class AppendWorkload:
+    """One latent-append step: N new tokens of width d_model written into a
+    cache of B sequences with T_cap row slots each."""
+    name: str
+    N: int
+    d_model: int
+    B: int
+    T_cap: int
+    paged: bool = True
+    cache_dtype: str = "fp8"
+    seed: int = 0
+
+
+APPEND_WORKLOADS = {
+    # one decode step of DeepSeek-V3 shape: 64 sequences append one token each
+    # into a paged FP8 cache of 4096 slots per sequence
+    "latent_append": AppendWorkload("latent_append", N=64, d_model=D_MODEL, B=64, T_cap=4096, seed=7),
+}
+
+
+def generate_append(w: AppendWorkload, seed: Optional[int] = None, distinct: bool = True) -> dict:
+    """Draw x [N, d] ~ N(0, 1) and w_dkr [576, d] ~ N(0, 1/d) (bf16 bits), so
+    every projected value is about N(0, 1); token n goes to sequence
+    seq_id[n] (uniform) at a uniform position below T_cap, all (sequence,
+    position) slots distinct when ``distinct``.  Draw order: w_dkr, x,
+    seq_id, pos."""
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    w_dkr = to_bf16_bits(_normal(rng, (ROW, w.d_model), w.d_model ** -0.5))
+    x = to_bf16_bits(_normal(rng, (w.N, w.d_model), 1.0))
+    if distinct:
+        if w.N > w.B * w.T_cap:
+            raise ValueError("more tokens than slots")
+        slots = rng.choice(w.B * w.T_cap, size=w.N, replace=False)
+        seq_id = (slots // w.T_cap).astype(np.int32)
+        pos = (slots % w.T_cap).astype(np.int32)
+    else:
+        seq_id = rng.integers(0, w.B, size=w.N).astype(np.int32)
+        pos = rng.integers(0, w.T_cap, size=w.N).astype(np.int32)
+    return dict(workload=w, seed=seed, x=x, w_dkr=w_dkr, seq_id=seq_id, pos=pos)

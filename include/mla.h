@@ -276,6 +276,48 @@ mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv,
                             float softmax_scale, int32_t causal, void* out,
                             void* workspace, size_t ws_bytes, void* stream);
 
+/* Latent append -- the step that produces the cached row of each new token
+ * ("Why MLA and MTP Fight Each Other", section 3: the hidden state x is
+ * compressed to the 512-wide latent c = x W_DKV that the cache stores;
+ * Appendix A there and "MLA, dim by dim", "Why RoPE Gets in the Way": a
+ * 64-wide rope key, rotated by the token's position and shared by all heads,
+ * is stored beside the latent).  For token n with hidden state x[n]:
+ *   row[c]       = sum_k x[n, k] * w_dkr[c, k]                      (c < 512)
+ *   key[r]       = sum_k x[n, k] * w_dkr[512 + r, k]                (r < 64)
+ *   row[512 + r] = key turned pairwise: for i < 32 and
+ *                  a = pos[n] * rope_base^(-2 i / 64),
+ *                  row[512 + 2i]     = key[2i] cos a - key[2i+1] sin a,
+ *                  row[512 + 2i + 1] = key[2i] sin a + key[2i+1] cos a
+ * (the pages leave the rotation's pairing and frequencies unwritten; this is
+ * the rotary embedding on consecutive pairs).  The row is stored at position
+ * pos[n] of sequence seq_id[n] of the cache `kv` describes (contiguous
+ * [B, T_stride, 576] or paged through kv->block_table):
+ *   MLA_BF16      each value rounded to nearest even;
+ *   MLA_FP8_E4M3  scale = amax|row| / 448 (fp32, 1 for a zero row) written to
+ *                 kv->row_scale, codes = E4M3(row / scale) rounded to nearest
+ *                 even from the fp32 quotient, clamped to +-448, sign kept.
+ * The call WRITES kv->rows and kv->row_scale (the descriptor's const
+ * qualifiers describe the decode calls); kv->seqlens and kv->max_seqlen are
+ * not used (the caller advances its lengths).
+ *   x        bf16 [N, d_model]; w_dkr bf16 [576, d_model] (W_DKV^T in rows
+ *            0..511, the rope-key projection W_KR^T in rows 512..575, the
+ *            (out, in) order of a linear layer); d_model % 64 == 0.
+ *   seq_id, pos  int32 [N].  A token whose seq_id is outside [0, B), whose
+ *            pos is outside [0, T_stride) (contiguous) or [0, max_blocks * 64)
+ *            (paged), or whose block-table entry is negative writes nothing.
+ *            Two tokens with the same slot race.
+ *   rope_base  finite and > 0 (10000 in the original rotary embedding).
+ *   workspace  ws_bytes >= mla_append_workspace_bytes(N, d_model): fp32
+ *            split-K partial rows, overwritten by the call.
+ * Products accumulate in fp32 on the matrix cores; the rotation angles and
+ * their sines and cosines are computed in fp64.  0 from
+ * mla_append_workspace_bytes means an invalid size. */
+size_t mla_append_workspace_bytes(int32_t N, int32_t d_model);
+mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_t d_model,
+                             const int32_t* seq_id, const int32_t* pos, float rope_base,
+                             const mla_kv_desc* kv, int32_t B, void* workspace,
+                             size_t ws_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host). */
 const char* mla_status_string(mla_status s);
 

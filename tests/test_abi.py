@@ -173,3 +173,31 @@ def test_sparse_rejects_bad_arguments(m):
     sa = m._lib.mla_sparse_decode_attn
     assert sa(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, None, 2, None, 0x5000, need, 0,
               None) == ARG
+
+
+def test_append_workspace_and_rejects_bad_arguments(m):
+    wsb = m._lib.mla_append_workspace_bytes
+    # d_model 7168 = 112 chunks of 64; 64 tokens: 256 / 18 column blocks -> 15
+    # splits asked, 8 chunks each -> 14 splits: 14 x 64 x 576 fp32 partial rows
+    assert wsb(64, 7168) == 14 * 64 * 576 * 4
+    assert wsb(1, 64) == 576 * 4                     # one split of one chunk (2304 B, already 256-aligned)
+    assert wsb(0, 7168) == 0 and wsb(64, 7160) == 0 and wsb(64, 7168 + 16) == 0 and wsb(64, 0) == 0
+    ap = m._lib.mla_latent_append
+    need = wsb(4, 256)
+    good = dict(x=0x1000, w=0x2000, N=4, d=256, sid=0x3000, pos=0x4000, base=10000.0, B=2, ws=0x5000, wsb=need)
+
+    def call(kv=None, **kw):
+        a = dict(good, **kw)
+        return ap(a["x"], a["w"], a["N"], a["d"], a["sid"], a["pos"], a["base"],
+                  None if kv is False else ctypes.byref(kv or _kv()), a["B"], a["ws"], a["wsb"], None)
+    assert call(x=None) == ARG and call(w=None) == ARG and call(sid=None) == ARG and call(pos=None) == ARG
+    assert call(kv=False) == ARG
+    assert call(N=0) == ARG and call(d=100) == ARG and call(B=0) == ARG
+    assert call(base=0.0) == ARG and call(base=float("nan")) == ARG and call(base=-2.0) == ARG
+    assert call(kv=_kv(rows=None)) == ARG
+    assert call(kv=_kv(dtype=1)) == ARG                                  # fp8 without scales
+    assert call(kv=_kv(row_scale=0x6000)) == ARG                         # bf16 with scales
+    assert call(kv=_kv(T_stride=0)) == ARG
+    assert call(kv=_kv(block_table=0x7000, block_size=32, max_blocks=4)) == UNSUP
+    assert call(kv=_kv(block_table=0x7000, block_size=64, max_blocks=0)) == ARG
+    assert call(wsb=need - 1) == WS and call(ws=None) == WS

@@ -1,0 +1,228 @@
+"""Latent append through the C ABI against the fp64 oracle (GPU).
+
+Exact cases (one-hot hidden states at position 0, where every product is
+exact in fp32) must match the oracle's roundings bit for bit, ties included.
+General cases check each stored value against the exact fp64 row within half
+a storage quantum plus a bound on fp32 accumulation error, that the FP8
+scale is amax / 448, and that no other slot of the cache changed.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import latent_append as A
+from oracle import mla_oracle as O
+from head_latent_attention_mla_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+BASE = 10000.0
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from head_latent_attention_mla_amd import mla as m
+    return m
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _make_cache(mla, B, T_cap, paged, fp8, seed, dead_block=False):
+    """A cache full of finite junk (every slot must keep it unless written)."""
+    rng = np.random.default_rng(seed)
+    n_rows = B * T_cap
+    if fp8:
+        rows = rng.integers(0, 0x7E, size=n_rows * 576, dtype=np.uint8)      # finite positive codes
+        scale = rng.uniform(0.5, 2.0, size=n_rows).astype(np.float32)
+    else:
+        rows = W.to_bf16_bits(rng.standard_normal(n_rows * 576))
+        scale = None
+    table = None
+    if paged:
+        shape = (n_rows // 64, 64, 576)
+        table = rng.permutation(n_rows // 64).astype(np.int32).reshape(B, T_cap // 64)
+        if dead_block:
+            table[0, 1] = -1
+    else:
+        shape = (B, T_cap, 576)
+    rows = rows.reshape(shape)
+    d_rows = torch.from_numpy(rows).cuda() if fp8 else _bf16_dev(rows)
+    d_scale = None if scale is None else torch.from_numpy(scale.reshape(shape[:2])).cuda()
+    cache = mla.LatentCache(rows=d_rows, seqlens=torch.full((B,), T_cap, dtype=torch.int32, device="cuda"),
+                            max_seqlen=T_cap, row_scale=d_scale,
+                            block_table=None if table is None else torch.from_numpy(table).cuda())
+    return cache, table
+
+
+def _snapshot(cache):
+    rows = cache.rows.view(torch.uint8) if cache.fp8 else cache.rows.view(torch.int16)
+    rows = rows.cpu().numpy().reshape(-1, 576)
+    scale = None if not cache.fp8 else cache.row_scale.cpu().numpy().reshape(-1)
+    return rows, scale
+
+
+def _slot_of(table, T_cap, b, p):
+    if table is None:
+        return b * T_cap + p
+    return int(table[b, p // 64]) * 64 + p % 64
+
+
+def _run(mla, x_bits, w_bits, seq_id, pos, cache):
+    mla.latent_append(_bf16_dev(x_bits), _bf16_dev(w_bits), torch.from_numpy(seq_id).cuda(),
+                      torch.from_numpy(pos).cuda(), cache, BASE)
+    torch.cuda.synchronize()
+
+
+def _quantum_e4m3(z):
+    a = np.maximum(np.abs(z), 2.0 ** -6)
+    return np.exp2(np.floor(np.log2(a)) - 3)
+
+
+def _check(got_rows, got_scale, exact, bound, fp8, what):
+    """got_rows [n, 576] stored codes/bits; exact [n, 576] f64; bound [n, 576]
+    the fp32 accumulation error allowed on each value."""
+    if not fp8:
+        dec = O.bf16_to_f64(got_rows.view(np.uint16))
+        a = np.abs(exact) + bound
+        ulp = np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 7)
+        err = np.abs(dec - exact)
+        bad = err > 0.5 * ulp + bound
+        assert not bad.any(), f"{what}: bf16 value off by {err[bad][:4]} (allowed {(0.5 * ulp + bound)[bad][:4]})"
+        return
+    amax = np.max(np.abs(exact), axis=1)
+    amax_err = np.max(bound, axis=1)
+    assert np.all(np.abs(got_scale.astype(np.float64) * 448.0 - amax) <= amax_err + 2.0 ** -22 * amax), \
+        f"{what}: scale not amax / 448"
+    sc = got_scale.astype(np.float64)[:, None]
+    z = exact / sc
+    zb = bound / sc
+    dec = O.e4m3_to_f64(got_rows.view(np.uint8))
+    allowed = 0.5 * _quantum_e4m3(np.minimum(np.abs(z) + zb, 448.0)) + zb + 2.0 ** -20
+    err = np.abs(dec - np.clip(z, -448.0, 448.0))
+    bad = err > allowed
+    assert not bad.any(), f"{what}: e4m3 value off by {err[bad][:4]} (allowed {allowed[bad][:4]})"
+
+
+def _bounds(x, w, d):
+    """Elementwise bound on the fp32 error of each stored value before its
+    storage rounding: dot products of length d summed over the k-splits,
+    then the rotation of the rope pairs (one fp32 rounding)."""
+    gamma = 2.0 ** -24 * (d / 16 + 64)
+    S = np.abs(x) @ np.abs(w).T
+    b = gamma * S
+    rope = b[:, 512:]
+    pair = rope[:, 0::2] + rope[:, 1::2]
+    b[:, 512:] = np.repeat(pair, 2, axis=1)
+    return b
+
+
+LAYOUTS = [(False, False), (True, False), (False, True), (True, True)]     # (paged, fp8)
+
+
+@pytest.mark.parametrize("paged,fp8", LAYOUTS)
+@pytest.mark.parametrize("N,d", [(1, 256), (37, 1088), (64, 7168), (150, 512)])
+def test_append_vs_oracle(mla, paged, fp8, N, d):
+    B, T_cap = 5, 256
+    wl = W.AppendWorkload("t", N=N, d_model=d, B=B, T_cap=T_cap, paged=paged,
+                          cache_dtype="fp8" if fp8 else "bf16", seed=90 + N)
+    inp = W.generate_append(wl)
+    print(f"[append] N={N} d={d} paged={paged} fp8={fp8}", flush=True)
+    cache, table = _make_cache(mla, B, T_cap, paged, fp8, seed=N + d)
+    before_rows, before_scale = _snapshot(cache)
+    _run(mla, inp["x"], inp["w_dkr"], inp["seq_id"], inp["pos"], cache)
+    after_rows, after_scale = _snapshot(cache)
+
+    x = O.bf16_to_f64(inp["x"])
+    w = O.bf16_to_f64(inp["w_dkr"])
+    exact = A.append_rows(x, w, inp["pos"], BASE)
+    slots = np.array([_slot_of(table, T_cap, int(b), int(p)) for b, p in zip(inp["seq_id"], inp["pos"])])
+    _check(after_rows[slots], None if not fp8 else after_scale[slots], exact, _bounds(x, w, d), fp8,
+           f"N={N} d={d} paged={paged} fp8={fp8}")
+    keep = np.ones(len(after_rows), bool)
+    keep[slots] = False
+    np.testing.assert_array_equal(after_rows[keep], before_rows[keep])
+    if fp8:
+        np.testing.assert_array_equal(after_scale[keep], before_scale[keep])
+
+
+@pytest.mark.parametrize("paged,fp8", LAYOUTS)
+def test_append_exact_inputs_bit_exact(mla, paged, fp8):
+    """One-hot hidden states at position 0: every stored value is an exact
+    fp32 product, so the stored bits are the oracle's roundings exactly."""
+    B, T_cap, d = 3, 128, 320
+    rng = np.random.default_rng(7)
+    w = rng.standard_normal((576, d))
+    # columns with bf16 and E4M3 ties: row 0 carries the magnitude 448 (so a
+    # unit one-hot input gives scale 1), the next rows exact midpoints
+    w[:, 0] = rng.standard_normal(576)
+    w[0, 0] = 448.0
+    w[1:8, 0] = [432.0, 1.0625, -1.1875, 2.0 ** -10, 3 * 2.0 ** -10, -2.0 ** -10, 40.0]
+    w_bits = W.to_bf16_bits(w)
+    w64 = O.bf16_to_f64(w_bits)
+    N = 6
+    x = np.zeros((N, d))
+    x[0, 0] = 1.0                     # E4M3 ties at scale 1
+    x[1, 5] = -2.0
+    x[2, 17] = 1.0 + 2.0 ** -7        # bf16 ties: (1 + 2^-7) * 8-bit weights
+    x[3, 300] = 0.5
+    x[4, 0] = 1.0 + 2.0 ** -7
+    x[5, 299] = -0.75
+    x_bits = W.to_bf16_bits(x)
+    seq_id = np.array([0, 1, 2, 0, 1, 2], np.int32)
+    pos = np.zeros(N, np.int32)        # position 0: the rotation is the identity
+    # tokens 0..2 go to position 0 of sequences 0..2; tokens 3..5 overwrite
+    # the same slots in a second call
+    cache, table = _make_cache(mla, B, T_cap, paged, fp8, seed=11)
+    for half in (slice(0, 3), slice(3, 6)):
+        _run(mla, x_bits[half], w_bits, seq_id[half], pos[half], cache)
+        rows, scale = _snapshot(cache)
+        exact = O.bf16_to_f64(x_bits[half]) @ w64.T
+        for i, b in enumerate(seq_id[half]):
+            s = _slot_of(table, T_cap, int(b), 0)
+            v = exact[i]
+            if not fp8:
+                np.testing.assert_array_equal(rows[s].view(np.uint16), A.bf16_nearest(v))
+            else:
+                sc = np.float32(np.float32(np.max(np.abs(v))) / np.float32(448.0))
+                assert scale[s] == sc
+                q = (v.astype(np.float32) / sc).astype(np.float64)       # the fp32 quotient
+                np.testing.assert_array_equal(rows[s], A.e4m3_nearest(q))
+
+
+def test_append_skips_invalid_slots(mla):
+    """Tokens with an out-of-range sequence or position, or a dead block,
+    write nothing; the valid ones in the same call are written."""
+    B, T_cap, d = 3, 192, 128
+    cache, table = _make_cache(mla, B, T_cap, True, True, seed=13, dead_block=True)
+    rng = np.random.default_rng(14)
+    x_bits = W.to_bf16_bits(rng.standard_normal((6, d)))
+    w_bits = W.to_bf16_bits(rng.standard_normal((576, d)) / np.sqrt(d))
+    seq_id = np.array([0, 3, -1, 0, 1, 2], np.int32)
+    pos = np.array([70, 5, 5, 192, -4, 191], np.int32)    # token 0 lands in the dead block
+    before_rows, before_scale = _snapshot(cache)
+    _run(mla, x_bits, w_bits, seq_id, pos, cache)
+    after_rows, after_scale = _snapshot(cache)
+    s5 = _slot_of(table, T_cap, 2, 191)
+    changed = np.nonzero(np.any(after_rows != before_rows, axis=1) | (after_scale != before_scale))[0]
+    assert changed.tolist() == [s5]
+    exact = A.append_rows(O.bf16_to_f64(x_bits[5:6]), O.bf16_to_f64(w_bits), pos[5:6], BASE)
+    _check(after_rows[[s5]], after_scale[[s5]], exact, _bounds(O.bf16_to_f64(x_bits[5:6]), O.bf16_to_f64(w_bits), d),
+           True, "valid token")
+
+
+def test_append_full_size(mla):
+    """64 tokens of width 7168 into a paged FP8 cache of 64 x 4096 slots."""
+    wl = W.APPEND_WORKLOADS["latent_append"]
+    inp = W.generate_append(wl)
+    print(f"[append] full {wl}", flush=True)
+    cache, table = _make_cache(mla, wl.B, wl.T_cap, wl.paged, wl.cache_dtype == "fp8", seed=15)
+    _run(mla, inp["x"], inp["w_dkr"], inp["seq_id"], inp["pos"], cache)
+    rows, scale = _snapshot(cache)
+    x = O.bf16_to_f64(inp["x"])
+    w = O.bf16_to_f64(inp["w_dkr"])
+    exact = A.append_rows(x, w, inp["pos"], BASE)
+    slots = np.array([_slot_of(table, wl.T_cap, int(b), int(p)) for b, p in zip(inp["seq_id"], inp["pos"])])
+    _check(rows[slots], scale[slots], exact, _bounds(x, w, wl.d_model), True, "full size")
