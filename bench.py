@@ -254,6 +254,105 @@ def append_main(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def prefill_flops(w, seqlens):
+    """Expand-path FLOPs of one call: the per-head expansion of every cached
+    row (2 T H d_c (d_k + d_v)) and 2 (192 + 128) per head and visible
+    (query, row) pair."""
+    expand = sum(2 * int(T) * w.H * 512 * 256 for T in seqlens)
+    pairs = 0
+    for T in seqlens:
+        T = int(T)
+        if w.causal:
+            pairs += sum(T - w.s_q + j + 1 for j in range(w.s_q))
+        else:
+            pairs += w.s_q * T
+    return expand, pairs * w.H * 2 * (192 + 128)
+
+
+def prefill_main(args, w):
+    """The expand (prefill) path alone: one call expands every cached row per
+    head and runs causal attention for all s_q query tokens.  MFMA-bound."""
+    import torch
+    from head_latent_attention_mla_amd import workloads as W
+    from head_latent_attention_mla_amd import mla
+
+    scale = 1.0 / math.sqrt(192.0)
+    print(f"[bench] generating {w}", file=sys.stderr, flush=True)
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, w_uk, w_uv, cache = W.to_torch(inp, dev)
+    out = torch.empty((w.B, w.s_q, w.H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(mla.prefill_workspace_bytes(w.B, w.s_q, w.H, cache.max_seqlen), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mla.prefill_expand(q, cache, w_uk, w_uv, scale, causal=w.causal, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    s = ms * 1e-3
+    f_expand, f_attn = prefill_flops(w, inp["seqlens"])
+    flops = f_expand + f_attn
+    tflops = flops / s / 1e12
+    rec = {
+        "metric": "MLA prefill (expand path) TFLOP/s (% MFMA roofline)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} prompts of {w.s_q} tokens, H={w.H}, "
+                               f"{'causal' if w.causal else 'non-causal'}, contiguous {w.cache_dtype} latent cache, "
+                               f"seed {w.seed}",
+                   "global_batch": w.B, "seq_len": w.s_q, "parallelism": "single GPU"},
+        "tokens_per_s": round(w.B * w.s_q / s, 1),
+        "roofline": {
+            "kernel": "prefill expand path (transpose_wuv + expand_kv_kernel + prefill_attn_kernel, one call)",
+            "bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops, "expand_flops": f_expand, "attention_flops": f_attn,
+            "avg_launch_us": round(ms * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        import numpy as np
+        from threadpoolctl import threadpool_info
+        import oracle
+        rng = np.random.default_rng(0)
+        done, fl, t_start = 0, 0, time.perf_counter()
+        while time.perf_counter() - t_start < min(args.cpu_seconds, 20.0) or done == 0:
+            b, h = int(rng.integers(w.B)), int(rng.integers(w.H))
+            oracle.naive_decode(inp, scale, causal=w.causal, pairs=[(b, h)])
+            one = w.with_(B=1, H=1)
+            e1, a1 = prefill_flops(one, [inp["seqlens"][b]])
+            fl += e1 + a1
+            done += 1
+        dt = time.perf_counter() - t_start
+        rec["cpu_baseline"] = {
+            "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1]), "kind": "oracle",
+            "sample": f"{done} random (sequence, head) pairs of the {w.name} workload, fp64 numpy expand-then-attend, "
+                      f"{dt:.1f} s; value = expand-path FLOPs of those pairs per second",
+        }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +387,9 @@ def main():
         append_main(args, W.APPEND_WORKLOADS[args.workload])
         return
     w = W.WORKLOADS[args.workload]
+    if w.name == "prefill":
+        prefill_main(args, w)
+        return
     scale = 1.0 / math.sqrt(192.0)
     print(f"[bench] generating {w}", file=sys.stderr, flush=True)
     inp = W.generate(w)

@@ -91,6 +91,75 @@ bool append_split(int32_t N, int32_t d_model, int32_t* ks_count, int32_t* chunks
   return true;
 }
 
+struct PrefillLayout {
+  int32_t T_pad;
+  size_t wuvt_off, kn_off, v_off, rope_off, bytes;
+};
+
+// Workspace of the expand path: W_UV^T per head, then K_nope and V
+// [B, H, T_pad, 128] and the rope keys [B, T_pad, 64] (bf16), 256-aligned.
+bool prefill_layout(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, PrefillLayout* l) {
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || s_q > max_seqlen) return false;
+  if (B > (1 << 16) || H > (1 << 12) || max_seqlen > (1 << 24)) return false;
+  if ((int64_t)B * s_q * H > (1 << 30)) return false;
+  l->T_pad = (int32_t)((max_seqlen + 127) / 128 * 128);
+  const size_t kv = (size_t)B * H * l->T_pad * mla::D_NOPE * sizeof(uint16_t);
+  l->wuvt_off = 0;
+  l->kn_off = align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t));
+  l->v_off = l->kn_off + align_up(kv);
+  l->rope_off = l->v_off + align_up(kv);
+  l->bytes = l->rope_off + align_up((size_t)B * l->T_pad * mla::D_ROPE * sizeof(uint16_t));
+  return true;
+}
+
+// The query-token count from which expanding the cache is cheaper in FLOPs
+// than absorbing: S*(L) = L d_c (d_k + d_v) / (d_c (d_k + d_v) + L (2 d_c - d_k - d_v))
+// with d_k = d_v = 128 ("Why MLA and MTP Fight Each Other", section 5.6; the
+// rope segment adds the same 64 to both per-pair costs and cancels).
+double crossover_tokens(int32_t L) {
+  const double expand = (double)mla::D_C * (mla::D_NOPE + mla::D_V);
+  return (double)L * expand / (expand + (double)L * (2.0 * mla::D_C - mla::D_NOPE - mla::D_V));
+}
+
+bool use_expand(int32_t s_q, int32_t max_seqlen) { return (double)s_q >= crossover_tokens(max_seqlen); }
+
+mla_status prefill_impl(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv, int32_t B,
+                        int32_t s_q, int32_t H, float softmax_scale, int32_t causal, void* out, void* workspace,
+                        size_t ws_bytes, hipStream_t st) {
+  if (q == nullptr || w_uk == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  PrefillLayout l;
+  if (!prefill_layout(B, s_q, H, kv->max_seqlen, &l)) return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < l.bytes) return MLA_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  mla::PrefillParams p{};
+  p.q = (const uint16_t*)q;
+  p.rows = kv->rows;
+  p.row_scale = kv->row_scale;
+  p.block_table = kv->block_table;
+  p.seqlens = kv->seqlens;
+  p.w_uk = (const uint16_t*)w_uk;
+  p.w_uv = (const uint16_t*)w_uv;
+  p.w_uvt = (uint16_t*)(ws + l.wuvt_off);
+  p.k_nope = (uint16_t*)(ws + l.kn_off);
+  p.v = (uint16_t*)(ws + l.v_off);
+  p.rope = (uint16_t*)(ws + l.rope_off);
+  p.out = (uint16_t*)out;
+  p.T_stride = kv->T_stride;
+  p.max_blocks = kv->max_blocks;
+  p.B = B;
+  p.s_q = s_q;
+  p.H = H;
+  p.T_pad = l.T_pad;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.causal = causal;
+  p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  return hip_status(mla::launch_prefill(p, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -414,5 +483,62 @@ mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_
   return hip_status(mla::launch_append(p, (hipStream_t)stream));
 }
 
+size_t mla_prefill_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
+  PrefillLayout l;
+  return prefill_layout(B, s_q, H, max_seqlen, &l) ? l.bytes : 0;
+}
+
+mla_status mla_prefill_expand(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
+                              int32_t B, int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
+                              void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(q, kv, w_uk, w_uv, B, s_q, H, softmax_scale, causal, out, workspace, ws_bytes,
+                      (hipStream_t)stream);
+}
+
+int32_t mla_attend_uses_expand(int32_t s_q, int32_t max_seqlen) {
+  if (s_q <= 0 || max_seqlen <= 0) return -1;
+  return use_expand(s_q, max_seqlen) ? 1 : 0;
+}
+
+size_t mla_attend_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0) return 0;
+  if (use_expand(s_q, max_seqlen)) return mla_prefill_workspace_bytes(B, s_q, H, max_seqlen);
+  if ((int64_t)B * s_q * H > (1 << 26)) return 0;
+  Plan pl;
+  if (!make_plan(B, s_q, H, max_seqlen, 0, &pl)) return 0;
+  return align_up((size_t)B * s_q * H * mla::ROWW * sizeof(uint16_t)) + pl.ws_bytes;
+}
+
+mla_status mla_attend(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv, int32_t B,
+                      int32_t s_q, int32_t H, float softmax_scale, int32_t causal, void* out, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  if (kv == nullptr || q == nullptr || w_uk == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0 || kv->max_seqlen <= 0) return MLA_ERR_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  if (use_expand(s_q, kv->max_seqlen))
+    return prefill_impl(q, kv, w_uk, w_uv, B, s_q, H, softmax_scale, causal, out, workspace, ws_bytes, st);
+  // absorbed: q_lat in the workspace, then the split-T scan and the fused
+  // merge + W_UV projection on the rest of it
+  if ((int64_t)B * s_q * H > (1 << 26)) return MLA_ERR_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  const size_t need = mla_attend_workspace_bytes(B, s_q, H, kv->max_seqlen);
+  if (need == 0) return MLA_ERR_ARG;
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  const size_t ql_bytes = align_up((size_t)B * s_q * H * mla::ROWW * sizeof(uint16_t));
+  void* q_lat = workspace;
+  void* dws = (char*)workspace + ql_bytes;
+  const size_t dws_bytes = ws_bytes - ql_bytes;
+  mla_status s = mla_absorb_q(q, w_uk, q_lat, B * s_q, H, mla::D_NOPE, mla::D_ROPE, mla::D_C, stream);
+  if (s != MLA_OK) return s;
+  s = decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, dws, dws_bytes, 0, st);
+  if (s != MLA_OK) return s;
+  return mla_decode_combine_out(B, s_q, H, kv->max_seqlen, 0, dws, dws_bytes, w_uv, out, nullptr, MLA_FP32,
+                                nullptr, stream);
+}
+
 }  // extern "C"
+
 

@@ -95,6 +95,30 @@ struct AppendParams {
   int32_t fp8;
 };
 
+// One call of the expand (prefill) path: expand every cached row per head
+// into K_nope and V, then causal flash attention with the 192-wide queries.
+struct PrefillParams {
+  const uint16_t* q;            // bf16 [B, s_q, H, 192]
+  const void* rows;             // cache rows (contiguous or pool), bf16 or e4m3
+  const float* row_scale;       // e4m3 only
+  const int32_t* block_table;   // paged only (else null)
+  const int32_t* seqlens;       // [B]
+  const uint16_t* w_uk;         // bf16 [H, 128, 512]
+  const uint16_t* w_uv;         // bf16 [H, 512, 128]
+  uint16_t* w_uvt;              // workspace: bf16 [H, 128, 512], W_UV per head transposed
+  uint16_t* k_nope;             // workspace: bf16 [B, H, T_pad, 128]
+  uint16_t* v;                  // workspace: bf16 [B, H, T_pad, 128]
+  uint16_t* rope;               // workspace: bf16 [B, T_pad, 64]
+  uint16_t* out;                // bf16 [B, s_q, H, 128]
+  int64_t T_stride;
+  int32_t max_blocks;
+  int32_t B, s_q, H;
+  int32_t T_pad;                // rows per sequence in the expanded buffers (multiple of 128)
+  float scale_log2;
+  int32_t causal;
+  int32_t fp8;
+};
+
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
@@ -109,5 +133,7 @@ hipError_t launch_combine_out(const float* part_o, const float* part_lse, const 
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream);
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_transpose_wuv(const uint16_t* w_uv, uint16_t* w_uvt, int H, hipStream_t stream);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -205,10 +205,13 @@ __global__ __launch_bounds__(256) void naive_decode_kernel(NaiveParams p) {
 
 }  // namespace
 
+hipError_t launch_transpose_wuv(const uint16_t* w_uv, uint16_t* w_uvt, int H, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_wuv_kernel, dim3(D_C / 64, D_V / 64, H), dim3(256), 0, stream, w_uv, w_uvt);
+  return hipGetLastError();
+}
+
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(transpose_wuv_kernel, dim3(D_C / 64, D_V / 64, p.H), dim3(256), 0, stream, p.w_uv,
-                     p.w_uvt);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(naive_decode_kernel, dim3(p.H, p.B), dim3(256), 0, stream, p);
   return hipGetLastError();

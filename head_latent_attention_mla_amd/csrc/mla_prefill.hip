@@ -1,0 +1,383 @@
+// Prefill by expansion: the other bracketing of the same attention
+// ("Why MLA and MTP Fight Each Other", sections 5.5 and 5.6: with many query
+// tokens per cached row the per-row expansion is shared by all of them and the
+// narrower per-pair contraction wins; "MLA, dim by dim", "MLA Prefill": form
+// K = C W_UK and V = C W_UV once, then run ordinary attention over them).
+//
+// Two kernels:
+//   expand_kv_kernel   per (128 cached rows, head, sequence): K_nope^T and
+//       V^T tiles = W rows x C^T on MFMA (both operands straight from memory,
+//       contracted dimension contiguous), rounded to bf16 into
+//       [B, H, T_pad, 128]; the head-0 work-groups also copy the rows' rope
+//       keys to [B, T_pad, 64].  Rows past a sequence's end are written as 0.
+//   prefill_attn_kernel  per (128 query rows, head, sequence): causal flash
+//       attention.  Each wave owns 32 query rows: S^T = K Q^T (the K tile from
+//       LDS, the query rows held in registers), an online softmax per row,
+//       and O^T += V^T P^T with the probabilities kept in registers (the
+//       score accumulator layout is already the value product's B operand,
+//       up to a fixed permutation of the 16 rows of each k-step that the
+//       transposed V reads follow).  K, rope key and V tiles of 64 rows reach
+//       LDS by direct loads, double-buffered; 80 KB of LDS lets two
+//       work-groups share a compute unit, so one's softmax overlaps the
+//       other's matrix products.
+#include "mla_common.h"
+#include "mla_internal.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int KT = 64;                        // cached rows per attention tile
+constexpr int QT = 128;                       // query rows per attention work-group
+constexpr int ET = 128;                       // cached rows per expansion work-group
+constexpr int KN_BYTES = KT * D_NOPE * 2;     // 16 KB: K_nope tile
+constexpr int KR_BYTES = KT * D_ROPE * 2;     // 8 KB: rope key tile
+constexpr int V_BYTES = KT * D_V * 2;         // 16 KB: V tile
+constexpr int BUF_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
+constexpr float REF_STEP = 8.0f;              // softmax reference moves when the max passes it by 2^8
+
+__device__ __forceinline__ i16x8 ld16(const void* p) { return *(const i16x8*)p; }
+
+// the row of sequence b at position t in the cache (element index of its first value)
+__device__ __forceinline__ int64_t cache_row(const PrefillParams& p, int b, int t) {
+  if (p.block_table != nullptr) return (int64_t)p.block_table[(int64_t)b * p.max_blocks + (t >> 6)] * 64 + (t & 63);
+  return (int64_t)b * p.T_stride + t;
+}
+
+// 16 consecutive e4m3 codes times the row scale -> two bf16x8 fragments
+__device__ __forceinline__ void dequant16(u32x4 w, float s, i16x8& lo, i16x8& hi) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
+    i16x8& o = d < 2 ? lo : hi;
+    const int e = 4 * (d & 1);
+    o[e + 0] = (short)bf16_bits(to_bf16(a[0] * s));
+    o[e + 1] = (short)bf16_bits(to_bf16(a[1] * s));
+    o[e + 2] = (short)bf16_bits(to_bf16(c[0] * s));
+    o[e + 3] = (short)bf16_bits(to_bf16(c[1] * s));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// expansion.  Wave w: output columns 64 (w & 1) .. + 63 of K_nope (w < 2) or
+// of V (w >= 2), all 128 rows of the tile: 2 column blocks x 4 row blocks of
+// 32 x 32.  D[n][t] = sum_c W[n][c] C[t][c]: A = weight rows, B = cached rows.
+// Within each 64-wide chunk of c the order is permuted alike for both
+// operands (lane half h holds c = 32 h .. 32 h + 31; MFMA j takes 8 j .. 8 j
+// + 7), so every lane reads 64 contiguous bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
+  const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int T = p.seqlens[b];
+  const int t0 = tt * ET;
+  const bool is_v = wave >= 2;
+  const uint16_t* W = (is_v ? p.w_uvt : p.w_uk) + (int64_t)h * D_NOPE * D_C;
+  const int n0 = 64 * (wave & 1);
+
+  // cached rows of this lane for the 4 row blocks (clamped into the sequence:
+  // rows past its end are computed from a real row and stored as zeros)
+  int64_t crow[4];
+  float csc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = min(t0 + 32 * rb + l32, T - 1);
+    crow[rb] = cache_row(p, b, t);
+    csc[rb] = p.fp8 ? p.row_scale[crow[rb]] : 1.0f;
+  }
+  const uint16_t* wr0 = W + (int64_t)(n0 + l32) * D_C + 32 * half;
+  const uint16_t* wr1 = W + (int64_t)(n0 + 32 + l32) * D_C + 32 * half;
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  for (int ch = 0; ch < D_C / 64; ++ch) {
+    i16x8 a[2][4], bb[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[0][j] = ld16(wr0 + ch * 64 + 8 * j);
+      a[1][j] = ld16(wr1 + ch * 64 + 8 * j);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if (p.fp8) {
+        const uint8_t* src = (const uint8_t*)p.rows + crow[rb] * ROWW + ch * 64 + 32 * half;
+        const u32x4 w0 = *(const u32x4*)src;
+        const u32x4 w1 = *(const u32x4*)(src + 16);
+        dequant16(w0, csc[rb], bb[rb][0], bb[rb][1]);
+        dequant16(w1, csc[rb], bb[rb][2], bb[rb][3]);
+      } else {
+        const uint16_t* src = (const uint16_t*)p.rows + crow[rb] * ROWW + ch * 64 + 32 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bb[rb][j] = ld16(src + 8 * j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          acc[cb][rb] = mfma32(__builtin_bit_cast(bf16x8, a[cb][j]), __builtin_bit_cast(bf16x8, bb[rb][j]),
+                               acc[cb][rb]);
+  }
+
+  // lane holds D[n = 32 cb + 8 g + 4 half + e][t = 32 rb + l32], e < 4: four
+  // consecutive outputs of one row, stored as 8 bytes
+  uint16_t* dst = (is_v ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = 32 * rb + l32;
+    const bool live = t0 + t < T;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint64_t v = 0;
+        if (live) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[cb][rb][4 * g + e])) << (16 * e);
+        }
+        *(uint64_t*)(dst + (int64_t)t * D_NOPE + n0 + 32 * cb + 8 * g + 4 * half) = v;
+      }
+  }
+
+  // rope keys of the tile's rows (head-0 work-groups): 128 rows x 64 values
+  if (h == 0) {
+    uint16_t* rdst = p.rope + ((int64_t)b * p.T_pad + t0) * D_ROPE;
+    if (p.fp8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int idx = tid + 256 * i;            // row idx / 4, codes 16 (idx % 4) .. + 15
+        const int t = idx >> 2, qd = idx & 3;
+        i16x8 lo = {0, 0, 0, 0, 0, 0, 0, 0}, hi = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t0 + t < T) {
+          const int64_t r = cache_row(p, b, t0 + t);
+          dequant16(*(const u32x4*)((const uint8_t*)p.rows + r * ROWW + D_C + 16 * qd), p.row_scale[r], lo, hi);
+        }
+        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd) = lo;
+        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd + 8) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = tid + 256 * i;            // row idx / 8, values 8 (idx % 8) .. + 7
+        const int t = idx >> 3, c = idx & 7;
+        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (t0 + t < T) v = ld16((const uint16_t*)p.rows + cache_row(p, b, t0 + t) * ROWW + D_C + 8 * c);
+        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 8 * c) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
+  const int n_qt = gridDim.x;
+  const int qt = n_qt - 1 - (int)blockIdx.x;          // longest causal rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int T = p.seqlens[b];
+  const int H = p.H, s_q = p.s_q;
+
+  // own query row j (rows past s_q compute on row s_q - 1 and are not stored)
+  const int j_own = qt * QT + 32 * wave + l32;
+  const bool own_ok = j_own < s_q;
+  const int j_eff = min(j_own, s_q - 1);
+  const int lim = p.causal ? T - s_q + j_eff + 1 : T;              // visible rows 0 .. lim - 1
+  const int j_last = min(qt * QT + QT - 1, s_q - 1);
+  const int lim_wg = p.causal ? T - s_q + j_last + 1 : T;
+  const int n_tiles = (lim_wg + KT - 1) / KT;
+
+  bf16x8 qf[D_QK / 16];
+  {
+    const uint16_t* qrow = p.q + (((int64_t)b * s_q + j_eff) * H + h) * D_QK + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D_QK / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(qrow + 16 * ks));
+  }
+
+  // ---- direct-to-LDS tile loads.  Region rows hold R chunks of 16 B (R = 16
+  // for K_nope and V, 8 for the rope key) with the chunk index XOR-swizzled by
+  // chunk_swz(row); a 1 KB load k fills slots 64 k + lane, so lane l fetches
+  // the chunk that lands there.
+  const int64_t bh = (int64_t)b * H + h;
+  const char* kn_base = (const char*)(p.k_nope + bh * p.T_pad * D_NOPE);
+  const char* v_base = (const char*)(p.v + bh * p.T_pad * D_V);
+  const char* r_base = (const char*)(p.rope + (int64_t)b * p.T_pad * D_ROPE);
+  uint32_t off16[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = 4 * k + (lane >> 4);
+    off16[k] = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ chunk_swz(t)));
+  }
+  const uint32_t off8 = (uint32_t)((lane >> 3) * 128 + 16 * ((lane & 7) ^ chunk_swz(lane >> 3)));
+  auto issue_tile = [&](int tile, int buf) {
+    const int64_t r0 = (int64_t)tile * KT;
+    const auto kn = __builtin_amdgcn_make_buffer_rsrc((void*)(kn_base + r0 * 256), (short)0, KN_BYTES, 0x00020000);
+    const auto vv = __builtin_amdgcn_make_buffer_rsrc((void*)(v_base + r0 * 256), (short)0, V_BYTES, 0x00020000);
+    const auto kr = __builtin_amdgcn_make_buffer_rsrc((void*)(r_base + r0 * 128), (short)0, KR_BYTES, 0x00020000);
+    char* dst = smem + buf * BUF_BYTES;
+    // wave w: K_nope and V loads 4 w .. 4 w + 3, rope loads 2 w, 2 w + 1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * wave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kn, (lds_void_t*)(dst + k * 1024), 16, off16[i & 1], k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vv, (lds_void_t*)(dst + KN_BYTES + KR_BYTES + k * 1024), 16,
+                                               off16[i & 1], k * 1024, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = 2 * wave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + KN_BYTES + k * 1024), 16, off8, k * 1024, 0, 0);
+    }
+  };
+
+  // score-phase reads: row l32 (+32), chunk 2 ks + half, XOR-swizzled
+  const int sw = chunk_swz(l32);
+  uint32_t qo_n[4], qo_r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    qo_n[i] = l32 * 256 + 16 * ((2 * i + half) ^ sw);
+    qo_r[i] = KN_BYTES + l32 * 128 + 16 * ((2 * i + half) ^ sw);
+  }
+  // value-phase transposed reads (V^T fragments): lane reads row 16 kap + 4
+  // half + rsel (+ 8), columns 32 cb + 16 grp + csel
+  uint32_t pvo[2];
+  {
+    const int grp = (lane >> 4) & 1;
+    const int rsel = (lane & 15) >> 2;
+    const int csel = 4 * (lane & 3);
+    const int trow = 4 * half + rsel;
+    const int s2 = chunk_swz(trow);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int chunk = 4 * i + 2 * grp + (csel >> 3);
+      pvo[i] = KN_BYTES + KR_BYTES + trow * 256 + 16 * (chunk ^ s2) + (csel & 7) * 2;
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  float m_ref = -INFINITY, l_sum = 0.f;
+
+  if (n_tiles > 0) issue_tile(0, 0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // tile in LDS; the other buffer is free
+    if (tile + 1 < n_tiles) issue_tile(tile + 1, (tile + 1) & 1);
+    const int ts = tile * KT;
+
+    // ---- S^T = K Q^T: rows t = 32 sb + ..., columns = own query row
+    f32x16 s0 = {}, s1 = {};
+    const char* tbuf = smem + (tile & 1) * BUF_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < D_QK / 16; ++ks) {
+      i16x8 r0, r1;
+      if (ks < 8) {
+        const char* a = tbuf + qo_n[ks & 3] + 128 * (ks >> 2);
+        r0 = *(const i16x8*)a;
+        r1 = *(const i16x8*)(a + 32 * 256);
+      } else {
+        const char* a = tbuf + qo_r[ks & 3];
+        r0 = *(const i16x8*)a;
+        r1 = *(const i16x8*)(a + 32 * 128);
+      }
+      s0 = mfma32(__builtin_bit_cast(bf16x8, r0), qf[ks], s0);
+      s1 = mfma32(__builtin_bit_cast(bf16x8, r1), qf[ks], s1);
+    }
+    // rows at or past the own limit do not count
+    if (__builtin_amdgcn_ballot_w64(ts + KT > lim) != 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
+        s0[r] = (t < lim) ? s0[r] : -INFINITY;
+        s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
+      }
+    }
+    float mraw = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
+    float ma, mb;
+    {
+      ma = mraw;
+      mb = mraw;
+      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(ma), "+v"(mb));
+    }
+    const float mx = fmaxf(ma, mb) * p.scale_log2;
+    // lazy reference: moves only when the maximum passes it by more than 2^8
+    // (the first tile always holds a visible row of every live query row)
+    const bool move = m_ref == -INFINITY || mx > m_ref + REF_STEP;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      const float m_new = move ? mx : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_sum *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[cb] *= alpha;
+      m_ref = m_new;
+    }
+    bf16x8 pk[2][2];
+    float lq = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const __bf16 p0 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, -m_ref)));
+      const __bf16 p1 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, -m_ref)));
+      pk[0][r >> 3][r & 7] = p0;
+      pk[1][r >> 3][r & 7] = p1;
+      lq += (float)p0 + (float)p1;
+    }
+    {
+      float a2 = lq, b2 = lq;
+      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a2), "+v"(b2));
+      l_sum += a2 + b2;
+    }
+
+    // ---- O^T += V^T P^T: 4 k-steps (16 rows each) x 4 column blocks
+#pragma unroll
+    for (int kap = 0; kap < 4; ++kap) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const char* a = tbuf + pvo[cb & 1] + 16 * kap * 256 + 128 * (cb >> 1);
+        acc[cb] = mfma32(join_tr(ds_read_tr16(a), ds_read_tr16(a + 8 * 256)), pk[kap >> 1][kap & 1], acc[cb]);
+      }
+    }
+  }
+
+  // ---- epilogue: out[b, j, h, dv] = O / l; lane holds dv = 32 cb + 8 g + 4 half + e
+  if (!own_ok) return;
+  const float inv = l_sum > 0.f ? 1.0f / l_sum : 0.f;
+  uint16_t* orow = p.out + (((int64_t)b * s_q + j_own) * H + h) * D_V;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint64_t v = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[cb][4 * g + e] * inv)) << (16 * e);
+      *(uint64_t*)(orow + 32 * cb + 8 * g + 4 * half) = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(expand_kv_kernel, dim3(p.T_pad / ET, p.H, p.B), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((p.s_q + QT - 1) / QT, p.H, p.B), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

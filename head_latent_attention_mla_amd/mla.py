@@ -72,6 +72,13 @@ SIGNATURES = {
     "mla_append_workspace_bytes": (_SZ, [_I32, _I32]),
     "mla_latent_append": (_I32, [_VP, _VP, _I32, _I32, _VP, _VP, _F32, ctypes.POINTER(KVDesc), _I32, _VP, _SZ,
                                  _VP]),
+    "mla_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_prefill_expand": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP,
+                                  _VP, _SZ, _VP]),
+    "mla_attend_uses_expand": (_I32, [_I32, _I32]),
+    "mla_attend_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_attend": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP, _VP, _SZ,
+                          _VP]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
 }
 
@@ -410,3 +417,60 @@ def latent_append(x: torch.Tensor, w_dkr: torch.Tensor, seq_id: torch.Tensor, po
     _check(_lib.mla_latent_append(_ptr(x), _ptr(w_dkr), N, d, _ptr(seq_id), _ptr(pos), float(rope_base),
                                   ctypes.byref(kv), cache.B, _ptr(workspace), workspace.numel(),
                                   _stream(stream)), "mla_latent_append")
+
+
+def prefill_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int) -> int:
+    return int(_lib.mla_prefill_workspace_bytes(B, s_q, H, max_seqlen))
+
+
+def _attend_args(q, cache, w_uk, w_uv, out):
+    B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
+    _require(q, "q", torch.bfloat16, (B, s_q, H, D_NOPE + D_ROPE))
+    _require(w_uk, "w_uk", torch.bfloat16, (H, D_NOPE, D_C))
+    _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
+    kv = cache.desc()
+    if out is None:
+        out = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=q.device)
+    _require(out, "out", torch.bfloat16, (B, s_q, H, D_V))
+    return B, s_q, H, kv, out
+
+
+def prefill_expand(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+                   scale: float = DEFAULT_SCALE, causal: bool = True, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Expand path: every cached row expanded per head into K and V, then
+    attention with the 192-wide queries. Same I/O as decode()/naive_decode()."""
+    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out)
+    need = prefill_workspace_bytes(B, s_q, H, cache.max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.mla_prefill_expand(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
+                                   int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(),
+                                   _stream(stream)), "mla_prefill_expand")
+    return out
+
+
+def attend_uses_expand(s_q: int, max_seqlen: int) -> bool:
+    r = int(_lib.mla_attend_uses_expand(s_q, max_seqlen))
+    if r < 0:
+        raise ValueError("invalid sizes")
+    return bool(r)
+
+
+def attend_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int) -> int:
+    return int(_lib.mla_attend_workspace_bytes(B, s_q, H, max_seqlen))
+
+
+def attend(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
+           scale: float = DEFAULT_SCALE, causal: bool = True, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Absorbed or expand path, whichever costs fewer FLOPs for s_q query
+    tokens against max_seqlen cached rows."""
+    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out)
+    need = attend_workspace_bytes(B, s_q, H, cache.max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.mla_attend(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
+                           int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "mla_attend")
+    return out

@@ -86,6 +86,8 @@ WORKLOADS = {
     # Sparse top-k decode: 2048 of 16384 cached rows selected per sequence.
     "sparse_topk": Workload("sparse_topk", B=64, H=128, s_q=1, causal=False, T=16384,
                             topk=2048, seed=6),
+    # prefill of two 4096-token prompts: every cached row is also a query row
+    "prefill": Workload("prefill", B=2, H=128, s_q=4096, causal=True, T=4096, seed=8),
 }
 
 

@@ -318,6 +318,43 @@ mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_
                              const mla_kv_desc* kv, int32_t B, void* workspace,
                              size_t ws_bytes, void* stream);
 
+/* Prefill by expansion -- the other bracketing ("Why MLA and MTP Fight Each
+ * Other", sections 5.5-5.6: with many query tokens per cached row, expanding
+ * every row once into per-head keys and values and attending over them costs
+ * fewer FLOPs than absorbing; "MLA, dim by dim", "MLA Prefill": materialise
+ * K = C W_UK and V = C W_UV, then run standard attention).  Same inputs,
+ * outputs and masking as mla_naive_decode (and as steps 1-4 chained):
+ *   K_nope[t, h, :] = W_UK[h] row_t[0:512],  V[t, h, :] = row_t[0:512]^T W_UV[h]
+ *   key_t = [K_nope[t, h, :] | row_t[512:576]]
+ *   out[b, j, h, :] = sum_{t visible} softmax_t(scale * <q[b,j,h,:], key_t>) V[t, h, :]
+ * with the causal rule of mla_decode_attn.  Keys and values are rounded to
+ * bf16 in the workspace (FP8 rows are dequantised first); scores, softmax and
+ * the value sum accumulate in fp32 on the matrix cores.
+ *   q        bf16 [B, s_q, H, 192];  out  bf16 [B, s_q, H, 128]
+ *   workspace  ws_bytes >= mla_prefill_workspace_bytes(B, s_q, H, max_seqlen):
+ *            W_UV^T, K_nope and V [B, H, T_pad, 128] and the rope keys
+ *            [B, T_pad, 64], T_pad = max_seqlen rounded up to 128.
+ * s_q <= max_seqlen; 0 from mla_prefill_workspace_bytes means an invalid size. */
+size_t mla_prefill_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
+mla_status mla_prefill_expand(const void* q, const mla_kv_desc* kv, const void* w_uk,
+                              const void* w_uv, int32_t B, int32_t s_q, int32_t H,
+                              float softmax_scale, int32_t causal, void* out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Dispatch between the two bracketings by their FLOP counts ("Why MLA and MTP
+ * Fight Each Other", section 5.6): the expand path is used when
+ *   s_q >= S*(L) = L d_c (d_k + d_v) / (d_c (d_k + d_v) + L (2 d_c - d_k - d_v)),
+ * L = max_seqlen (S* is 128 at L = 512 and tends to 170.7), else the absorbed
+ * path (mla_absorb_q, mla_decode_partial, mla_decode_combine_out).
+ * mla_attend_uses_expand returns 1 (expand), 0 (absorbed) or -1 (bad sizes).
+ * mla_attend takes the inputs and output of mla_prefill_expand and a
+ * workspace of mla_attend_workspace_bytes(...) for the path it picks. */
+int32_t mla_attend_uses_expand(int32_t s_q, int32_t max_seqlen);
+size_t mla_attend_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
+mla_status mla_attend(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
+                      int32_t B, int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
+                      void* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static, human-readable name of a status code (host). */
 const char* mla_status_string(mla_status s);
 

@@ -201,3 +201,36 @@ def test_append_workspace_and_rejects_bad_arguments(m):
     assert call(kv=_kv(block_table=0x7000, block_size=32, max_blocks=4)) == UNSUP
     assert call(kv=_kv(block_table=0x7000, block_size=64, max_blocks=0)) == ARG
     assert call(wsb=need - 1) == WS and call(ws=None) == WS
+
+
+def test_prefill_dispatch_and_workspace(m):
+    ue = m._lib.mla_attend_uses_expand
+    # S*(L) = 131072 L / (131072 + 768 L): 128 at L = 512, 163.84 at L = 4096,
+    # 0.994 at L = 1 (a single cached row: expanding wins already at s_q = 1)
+    assert ue(127, 512) == 0 and ue(128, 512) == 1
+    assert ue(163, 4096) == 0 and ue(164, 4096) == 1
+    assert ue(170, 1 << 20) == 0 and ue(171, 1 << 20) == 1
+    assert ue(1, 1) == 1 and ue(0, 5) == -1 and ue(3, 0) == -1
+    pw = m._lib.mla_prefill_workspace_bytes
+    # T_pad 384: W_UV^T 2 MiB, K_nope and V 2 x 16 x 384 x 128 x 2 B each, rope 2 x 384 x 64 x 2 B
+    assert pw(2, 300, 16, 300) == 2 * 2 ** 20 + 2 * 3 * 2 ** 20 + 98304
+    assert pw(2, 301, 16, 300) == 0 and pw(0, 1, 16, 300) == 0
+    aw = m._lib.mla_attend_workspace_bytes
+    assert aw(2, 300, 16, 300) == pw(2, 300, 16, 300)                      # expand path
+    q_lat = 2 * 4 * 16 * 576 * 2
+    assert aw(2, 4, 16, 300) == q_lat + m._lib.mla_decode_workspace_bytes(2, 4, 16, 300, 0)   # absorbed path
+    pe = m._lib.mla_prefill_expand
+    need = pw(2, 4, 16, 256)
+    args = [0x1000, ctypes.byref(_kv()), 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, need, None]
+
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return pe(*a)
+    assert call(0, None) == ARG and call(2, None) == ARG and call(3, None) == ARG and call(9, None) == ARG
+    assert call(7, 0.0) == ARG and call(8, 2) == ARG and call(5, 300) == ARG
+    assert call(1, ctypes.byref(_kv(rows=None))) == ARG
+    assert call(11, need - 1) == WS and call(10, None) == WS
+    at = m._lib.mla_attend
+    assert at(0x1000, ctypes.byref(_kv()), 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, 16, None) == WS
+    assert at(0x1000, None, 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, 1 << 30, None) == ARG

@@ -1,0 +1,90 @@
+"""Prefill by expansion and the S*-based dispatch, through the C ABI, against
+the fp64 oracle's naive (expand-then-attend) form -- which is this path's
+definition ("MLA, dim by dim", "MLA Prefill").  Bars as for decode: max-abs
+<= 2e-2 beyond the final bf16 output rounding and relative L2 <= 5e-3; FP8
+caches max-abs <= 6e-2."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from head_latent_attention_mla_amd import workloads as W
+
+from test_gpu_parity import SCALE, _assert_close, _f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from head_latent_attention_mla_amd import mla as m
+    return m
+
+
+CASES = dict(
+    # every cached row is a query row (prompt prefill), ragged last tiles
+    prompt=W.Workload("pf_prompt", B=2, H=16, s_q=300, causal=True, T=300, seed=61),
+    # chunked prefill: 200 new tokens after a 500-row prefix
+    chunk=W.Workload("pf_chunk", B=2, H=8, s_q=200, causal=True, T=700, seed=62),
+    noncausal=W.Workload("pf_full", B=1, H=16, s_q=129, causal=False, T=257, seed=63),
+    paged=W.Workload("pf_paged", B=3, H=8, s_q=150, causal=True, T_range=(150, 420), paged=True, seed=64),
+    fp8=W.Workload("pf_fp8", B=2, H=8, s_q=190, causal=True, T=190, cache_dtype="fp8", seed=65),
+    tiny_q=W.Workload("pf_one", B=2, H=16, s_q=1, causal=True, T=77, seed=66),
+)
+
+
+def _run(mla, inp, fn="prefill_expand"):
+    q, w_uk, w_uv, cache = W.to_torch(inp)
+    w = inp["workload"]
+    out = getattr(mla, fn)(q, cache, w_uk, w_uv, SCALE, causal=w.causal)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("kind", list(CASES))
+def test_prefill_expand_vs_oracle(mla, kind):
+    w = CASES[kind]
+    print(f"[prefill] {kind} {w}", flush=True)
+    inp = W.generate(w)
+    got = _f64(_run(mla, inp))
+    ref = O.naive_decode(inp, SCALE, causal=w.causal)
+    _assert_close(got, ref, fp8=w.cache_dtype == "fp8", what=kind)
+
+
+def test_prefill_matches_absorbed_path(mla):
+    """The two bracketings of the same attention agree (PIN: associativity)."""
+    w = W.Workload("pf_vs_abs", B=2, H=32, s_q=8, causal=True, T=520, seed=67)
+    inp = W.generate(w)
+    q, w_uk, w_uv, cache = W.to_torch(inp)
+    a = _f64(mla.prefill_expand(q, cache, w_uk, w_uv, SCALE, causal=True))
+    b = _f64(mla.decode(q, cache, w_uk, w_uv, SCALE, causal=True))
+    torch.cuda.synchronize()
+    ref = O.naive_decode(inp, SCALE, causal=True)
+    _assert_close(a, ref, what="expand")
+    _assert_close(b, ref, what="absorbed")
+
+
+@pytest.mark.parametrize("s_q,T", [(4, 600), (127, 512), (128, 512), (300, 300)])
+def test_attend_dispatch(mla, s_q, T):
+    """mla_attend picks the path by S*(L) and both give the oracle's result."""
+    expect_expand = s_q >= T * 131072 / (131072 + 768 * T)
+    assert mla.attend_uses_expand(s_q, T) == expect_expand
+    w = W.Workload("pf_dispatch", B=1, H=8, s_q=s_q, causal=True, T=T, seed=68 + s_q)
+    inp = W.generate(w)
+    got = _f64(_run(mla, inp, "attend"))
+    _assert_close(got, O.naive_decode(inp, SCALE, causal=True), what=f"attend s_q={s_q}")
+
+
+def test_prefill_full_size_sampled(mla):
+    """Two 4096-token prompts, 128 heads, causal; sampled (sequence, head)."""
+    w = W.WORKLOADS["prefill"]
+    print(f"[prefill] full {w}", flush=True)
+    inp = W.generate(w)
+    got = _f64(_run(mla, inp))
+    rng = np.random.default_rng(9)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(3)] + [(0, 0), (w.B - 1, w.H - 1)]
+    ref = O.naive_decode(inp, SCALE, causal=True, pairs=pairs)
+    for b, h in pairs:
+        _assert_close(got[b, :, h], ref[b, :, h], what=f"prefill full ({b},{h})")
