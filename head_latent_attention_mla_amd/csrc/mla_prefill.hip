@@ -180,11 +180,18 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
 // ---------------------------------------------------------------------------
 // attention
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, int n_qt, int n_items,
+                                                                int per_xcd) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * BUF_BYTES];
-  const int n_qt = gridDim.x;
-  const int qt = n_qt - 1 - (int)blockIdx.x;          // longest causal rows first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const uint32_t smem_a = lds_addr(smem);
+  // XCD-aware order: launch slot L runs on XCD L % 8; the query tiles of one
+  // (sequence, head) take consecutive items on one XCD, so its K and V tiles
+  // are fetched into that XCD's L2 once; within a head, longest causal rows first
+  const int item = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int qt = n_qt - 1 - item % n_qt;
+  const int h = (item / n_qt) % p.H;
+  const int b = item / (n_qt * p.H);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -274,28 +281,63 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
 
   if (n_tiles > 0) issue_tile(0, 0);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // tile in LDS; the other buffer is free
+    // tile in LDS (every wave's loads done); every wave is past the previous
+    // value phase, so the other buffer is free for the next tile
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (tile + 1 < n_tiles) issue_tile(tile + 1, (tile + 1) & 1);
+    const uint32_t tb = smem_a + (tile & 1) * BUF_BYTES;
     const int ts = tile * KT;
 
-    // ---- S^T = K Q^T: rows t = 32 sb + ..., columns = own query row
+    // ---- S^T = K Q^T: rows t = 32 sb + ..., columns = own query row.  LDS
+    // reads run QK_AHEAD k-steps ahead of the products (inline asm: the
+    // compiler would otherwise wait for the next tile's loads before them)
     f32x16 s0 = {}, s1 = {};
-    const char* tbuf = smem + (tile & 1) * BUF_BYTES;
+    {
+      uint32_t an[4], ar[4];
 #pragma unroll
-    for (int ks = 0; ks < D_QK / 16; ++ks) {
-      i16x8 r0, r1;
-      if (ks < 8) {
-        const char* a = tbuf + qo_n[ks & 3] + 128 * (ks >> 2);
-        r0 = *(const i16x8*)a;
-        r1 = *(const i16x8*)(a + 32 * 256);
-      } else {
-        const char* a = tbuf + qo_r[ks & 3];
-        r0 = *(const i16x8*)a;
-        r1 = *(const i16x8*)(a + 32 * 128);
+      for (int i = 0; i < 4; ++i) {
+        an[i] = tb + qo_n[i];
+        ar[i] = tb + qo_r[i];
       }
-      s0 = mfma32(__builtin_bit_cast(bf16x8, r0), qf[ks], s0);
-      s1 = mfma32(__builtin_bit_cast(bf16x8, r1), qf[ks], s1);
+      constexpr int QK_AHEAD = 3;
+      i16x8 ra[QK_AHEAD + 1][2];
+      auto issue_qk = [&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr int slot = ks % (QK_AHEAD + 1);
+        if constexpr (ks < 8) {
+          lds_read_b128<128 * (ks >> 2)>(ra[slot][0], an[ks & 3]);
+          lds_read_b128<128 * (ks >> 2) + 32 * 256>(ra[slot][1], an[ks & 3]);
+        } else {
+          lds_read_b128<0>(ra[slot][0], ar[ks & 3]);
+          lds_read_b128<32 * 128>(ra[slot][1], ar[ks & 3]);
+        }
+      };
+      static_for<0, QK_AHEAD>(issue_qk);
+      static_for<0, D_QK / 16>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr int NS = D_QK / 16;
+        constexpr int ahead = (NS - 1 - ks) < QK_AHEAD ? (NS - 1 - ks) : QK_AHEAD;
+        if constexpr (ks + QK_AHEAD < NS) issue_qk(std::integral_constant<int, ks + QK_AHEAD>{});
+        constexpr int slot = ks % (QK_AHEAD + 1);
+        wait_lgkm<2 * ahead>(ra[slot][0], ra[slot][1]);
+        s0 = mfma32(__builtin_bit_cast(bf16x8, ra[slot][0]), qf[ks], s0);
+        s1 = mfma32(__builtin_bit_cast(bf16x8, ra[slot][1]), qf[ks], s1);
+      });
     }
+    // the first two V^T fragments only need the tile: start them now
+    const uint32_t pv0 = tb + pvo[0], pv1 = tb + pvo[1];
+    i16x4 tr[3][2];
+    auto issue_a = [&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int kap = u >> 2, cb = u & 3;
+      constexpr int off = 16 * kap * 256 + 128 * (cb >> 1);
+      const uint32_t a = (cb & 1) ? pv1 : pv0;
+      lds_read_tr16<off>(tr[u % 3][0], a);
+      lds_read_tr16<off + 8 * 256>(tr[u % 3][1], a);
+    };
+    issue_a(std::integral_constant<int, 0>{});
+    issue_a(std::integral_constant<int, 1>{});
+
     // rows at or past the own limit do not count
     if (__builtin_amdgcn_ballot_w64(ts + KT > lim) != 0) {
 #pragma unroll
@@ -305,15 +347,16 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
         s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
       }
     }
-    float mraw = -INFINITY;
+    float mq[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, fmaxf(s0[r], s1[r]));
-    float ma, mb;
-    {
-      ma = mraw;
-      mb = mraw;
-      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(ma), "+v"(mb));
+    for (int c = 0; c < 4; ++c) {
+      const int r = 4 * c;
+      mq[c] = fmaxf(fmaxf(fmaxf(s0[r], s0[r + 1]), fmaxf(s0[r + 2], s0[r + 3])),
+                    fmaxf(fmaxf(s1[r], s1[r + 1]), fmaxf(s1[r + 2], s1[r + 3])));
     }
+    const float mraw = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    float ma = mraw, mb = mraw;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(ma), "+v"(mb));
     const float mx = fmaxf(ma, mb) * p.scale_log2;
     // lazy reference: moves only when the maximum passes it by more than 2^8
     // (the first tile always holds a visible row of every live query row)
@@ -327,30 +370,40 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p) {
       m_ref = m_new;
     }
     bf16x8 pk[2][2];
-    float lq = 0.f;
+    float lq[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const __bf16 p0 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, -m_ref)));
-      const __bf16 p1 = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, -m_ref)));
-      pk[0][r >> 3][r & 7] = p0;
-      pk[1][r >> 3][r & 7] = p1;
-      lq += (float)p0 + (float)p1;
+      pk[0][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, -m_ref)));
+      pk[1][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, -m_ref)));
     }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pk[sb][jj][e], pk[sb][jj][e + 1]};
+          lq[2 * jj + sb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq[2 * jj + sb], false);
+        }
     {
-      float a2 = lq, b2 = lq;
+      const float lsum = (lq[0] + lq[1]) + (lq[2] + lq[3]);
+      float a2 = lsum, b2 = lsum;
       asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a2), "+v"(b2));
       l_sum += a2 + b2;
     }
 
-    // ---- O^T += V^T P^T: 4 k-steps (16 rows each) x 4 column blocks
-#pragma unroll
-    for (int kap = 0; kap < 4; ++kap) {
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const char* a = tbuf + pvo[cb & 1] + 16 * kap * 256 + 128 * (cb >> 1);
-        acc[cb] = mfma32(join_tr(ds_read_tr16(a), ds_read_tr16(a + 8 * 256)), pk[kap >> 1][kap & 1], acc[cb]);
-      }
-    }
+    // ---- O^T += V^T P^T: 16 units u = 4 kap + cb (k-step kap of 16 rows,
+    // column block cb); the transposed V fragment of a unit is read two units
+    // ahead, every wait names the exact number of younger reads
+    static_for<0, 16>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int kap = u >> 2, cb = u & 3;
+      constexpr int younger = u == 15 ? 0 : 2;
+      wait_lgkm<younger>(tr[u % 3][0], tr[u % 3][1]);
+      if constexpr (u + 2 < 16) issue_a(std::integral_constant<int, u + 2>{});
+      acc[cb] = mfma32(join_tr(tr[u % 3][0], tr[u % 3][1]), pk[kap >> 1][kap & 1], acc[cb]);
+    });
   }
 
   // ---- epilogue: out[b, j, h, dv] = O / l; lane holds dv = 32 cb + 8 g + 4 half + e
@@ -376,7 +429,10 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(expand_kv_kernel, dim3(p.T_pad / ET, p.H, p.B), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((p.s_q + QT - 1) / QT, p.H, p.B), dim3(256), 0, stream, p);
+  const int n_qt = (p.s_q + QT - 1) / QT;
+  const int n_items = n_qt * p.H * p.B;
+  const int per_xcd = (n_items + 7) / 8;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(8 * per_xcd), dim3(256), 0, stream, p, n_qt, n_items, per_xcd);
   return hipGetLastError();
 }
 
