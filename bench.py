@@ -35,6 +35,7 @@ KERNEL_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_decode.hip",
 COPY_BYTES = 1 << 30         # read (and written) by the copy-kernel calibration run
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 N_COPIES = 3
 
 
@@ -359,6 +360,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--fp8-math", action="store_true",
+                    help="FP8 caches: run the scan with E4M3 matrix arithmetic (mla_decode_partial_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--naive-steps", type=int, default=3,
@@ -404,6 +407,10 @@ def main():
     B, s_q, H = w.B, w.s_q, w.H
     N = B * s_q
     sparse = w.topk is not None
+    f8m = bool(args.fp8_math)
+    if f8m and (w.cache_dtype != "fp8" or sparse):
+        print("--fp8-math needs a dense FP8-cache workload (fp8_cache)", file=sys.stderr)
+        sys.exit(2)
     selection = W.generate_selection(inp) if sparse else None
     q_lat = torch.empty((B, s_q, H, 576), dtype=torch.bfloat16, device=dev)
     out = torch.empty((B, s_q, H, 128), dtype=torch.bfloat16, device=dev)
@@ -428,7 +435,7 @@ def main():
         if sparse:
             mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws)
         else:
-            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws)
+            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws, fp8_math=f8m)
         if ev is not None:
             ev[2].record(stream)
         mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1))
@@ -465,6 +472,7 @@ def main():
     kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
 
     fp8 = w.cache_dtype == "fp8"
+    peak_mfma = FP8_PEAK_TFLOPS if f8m else BF16_PEAK_TFLOPS
     rows_read = [int(x) for x in (selection[1] if sparse else inp["seqlens"])]
     cnt = algorithmic_counts(B, s_q, H, rows_read, w.causal and not sparse,
                              cache_elem_bytes=1 if fp8 else 2, scale_bytes=4 if fp8 else 0)
@@ -478,13 +486,14 @@ def main():
     hbm_bound = (not fp8) and s_q == 1
     roofline = {
         "kernel": ("sparse gather + split-T scan (selected rows counted once)" if sparse
+                   else "decode_split_f8 (split-T latent scan, E4M3 arithmetic)" if f8m
                    else "decode_split (split-T latent scan)"),
         "bound": "hbm" if hbm_bound else "mfma",
         "achieved": round(scan_gbs if hbm_bound else scan_tflops, 1),
-        "peak": HBM_PEAK_GBS if hbm_bound else BF16_PEAK_TFLOPS,
+        "peak": HBM_PEAK_GBS if hbm_bound else peak_mfma,
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
-        "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / BF16_PEAK_TFLOPS), 4),
-        "traffic": None if sparse else measured_traffic(w.name),
+        "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / peak_mfma), 4),
+        "traffic": None if (sparse or f8m) else measured_traffic(w.name),
         "algorithmic_bytes_per_launch": cnt["bytes_scan"],
         "algorithmic_flops_per_launch": cnt["flops_scan"],
         "avg_launch_us": round(kern_us[names[1]], 2),
@@ -502,9 +511,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if f8m else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: B={B} H={H} s_q={s_q} T={w.T or w.T_range}"
+        "config": {"workload": f"{w.name}{' (E4M3 arithmetic)' if f8m else ''}: B={B} H={H} s_q={s_q} T={w.T or w.T_range}"
                                f"{f' top-{w.topk} selected' if sparse else ''} "
                                f"{'paged' if w.paged else 'contiguous'} {w.cache_dtype} latent cache [*, 576], "
                                f"{'causal' if w.causal else 'non-causal'}, seed {w.seed}",

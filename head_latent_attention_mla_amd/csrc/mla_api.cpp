@@ -202,7 +202,7 @@ namespace {
 
 mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                                int32_t H, float softmax_scale, int32_t causal, void* workspace,
-                               size_t ws_bytes, int32_t num_splits, hipStream_t st) {
+                               size_t ws_bytes, int32_t num_splits, hipStream_t st, bool fp8_math = false) {
   if (q_lat == nullptr) return MLA_ERR_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || num_splits < 0) return MLA_ERR_ARG;
   if (causal != 0 && causal != 1) return MLA_ERR_ARG;
@@ -237,6 +237,10 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   p.causal = causal;
   p.paged = kv->block_table != nullptr;
   p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  if (fp8_math) {
+    if (!p.fp8) return MLA_ERR_UNSUPPORTED;
+    return hip_status(mla::launch_decode_split_f8(p, st));
+  }
   return hip_status(mla::launch_decode_split(p, st));
 }
 
@@ -539,6 +543,14 @@ mla_status mla_attend(const void* q, const mla_kv_desc* kv, const void* w_uk, co
                                 nullptr, stream);
 }
 
+mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q, int32_t H,
+                                  float softmax_scale, int32_t causal, void* workspace, size_t ws_bytes,
+                                  int32_t num_splits, void* stream) {
+  return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace, ws_bytes, num_splits,
+                             (hipStream_t)stream, true);
+}
+
 }  // extern "C"
+
 
 

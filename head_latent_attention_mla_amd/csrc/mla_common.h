@@ -110,4 +110,58 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
+// Work-group barriers that wait only for what the barrier publishes.
+// __syncthreads() would also wait for the prefetch of the next tile (vmcnt).
+__device__ __forceinline__ void barrier_tile_ready() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// acc *= alpha on an accumulator that lives in AGPRs, one register at a time
+// (a plain vector multiply makes the register allocator move the whole block
+// through VGPRs).
+__device__ __forceinline__ void scale_acc(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = acc[i];
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t) : "v"(alpha));
+    acc[i] = x;
+  }
+}
+
+// lanes l and l ^ 32 hold the same query row: combine their values.
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another, so swapping x with a copy of x leaves {x[l], x[l ^ 32]} in
+// the two registers of every lane.  Issued as inline asm: the compiler's own
+// builtin is treated as returning two equal values and one gets folded away.
+// The s_nop padding covers the VALU-write -> permlane-read hazard and the
+// permlane-write -> VALU-read hazard.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// max of three, without the NaN-quieting the compiler adds around fmaxf on
+// values it cannot see (scores are finite or -inf)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
 }  // namespace mla

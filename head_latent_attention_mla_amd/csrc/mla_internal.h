@@ -120,6 +120,7 @@ struct PrefillParams {
 };
 
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
                           const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,

@@ -58,6 +58,8 @@ SIGNATURES = {
                                _VP, _VP, _SZ, _I32, _VP]),
     "mla_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ, _I32,
                                   _VP]),
+    "mla_decode_partial_fp8": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ,
+                                      _I32, _VP]),
     "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
     "mla_absorb_out": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
     "mla_decode_combine_out": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, _I32, _VP, _VP]),
@@ -231,17 +233,20 @@ def decode_attn(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_
 
 
 def decode_partial(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_SCALE, causal: bool = False,
-                   num_splits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Phase 1 of decode_attn: the split-T scan into a workspace (returned)."""
+                   num_splits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
+                   fp8_math: bool = False) -> torch.Tensor:
+    """Phase 1 of decode_attn: the split-T scan into a workspace (returned).
+    fp8_math (FP8 caches only): E4M3 matrix arithmetic (mla_decode_partial_fp8)."""
     B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
     _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
     kv = cache.desc()
     need = decode_workspace_bytes(B, s_q, H, cache.max_seqlen, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
-    _check(_lib.mla_decode_partial(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
-                                   _ptr(workspace), workspace.numel(), num_splits, _stream(stream)),
-           "mla_decode_partial")
+    fn, name = ((_lib.mla_decode_partial_fp8, "mla_decode_partial_fp8") if fp8_math
+                else (_lib.mla_decode_partial, "mla_decode_partial"))
+    _check(fn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
+              _ptr(workspace), workspace.numel(), num_splits, _stream(stream)), name)
     return workspace
 
 
@@ -296,14 +301,14 @@ def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
 
 def decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
            scale: float = DEFAULT_SCALE, causal: bool = False, o_dtype=torch.float32,
-           num_splits: int = 0, fused: bool = True, stream=None) -> torch.Tensor:
+           num_splits: int = 0, fused: bool = True, stream=None, fp8_math: bool = False) -> torch.Tensor:
     """Absorbed MLA decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16.
     fused: merge and project in one pass (mla_decode_combine_out); otherwise
     mla_decode_attn then mla_absorb_out.  Both give the same bits."""
     B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
     q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
-    if fused:
-        ws = decode_partial(q_lat, cache, scale, causal, num_splits, stream=stream)
+    if fused or fp8_math:
+        ws = decode_partial(q_lat, cache, scale, causal, num_splits, stream=stream, fp8_math=fp8_math)
         out = decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, num_splits, o_dtype, stream=stream)
         return out.view(B, s_q, H, D_V)
     o_lat, _ = decode_attn(q_lat, cache, scale, causal, o_dtype, num_splits, want_lse=False, stream=stream)

@@ -219,6 +219,22 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
                                   const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
                                   float* lse, void* stream);
 
+/* Step 2 with FP8 arithmetic ("Decode attention intensity is fixed at the
+ * query-to-KV head ratio...": FP8 halves the cache bytes; with FP8 matrix
+ * arithmetic the path is priced against the FP8 ridge).  Same arguments,
+ * workspace and partials as mla_decode_partial (merge them with
+ * mla_decode_combine or mla_decode_combine_out); kv->dtype must be
+ * MLA_FP8_E4M3 (else MLA_ERR_UNSUPPORTED).  The cached codes enter the matrix
+ * products as they are; each latent query row is quantised to E4M3 with its
+ * own scale amax/448, and the softmax weights times the row scales to E4M3
+ * (against a power-of-two normaliser), so the result approximates the exact
+ * attention to FP8 precision: about 1e-2 absolute on unit-scale outputs,
+ * within the FP8 bar of 6e-2. */
+mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int32_t B,
+                                  int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
+                                  void* workspace, size_t ws_bytes, int32_t num_splits,
+                                  void* stream);
+
 /* Sparse top-k decode ("Why MLA and MTP Fight Each Other", section 6: a
  * selector keeps the top-k cached latents and attention runs over those only,
  * gathered by index; the cost follows k instead of the context length).

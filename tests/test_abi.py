@@ -234,3 +234,12 @@ def test_prefill_dispatch_and_workspace(m):
     at = m._lib.mla_attend
     assert at(0x1000, ctypes.byref(_kv()), 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, 16, None) == WS
     assert at(0x1000, None, 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, 1 << 30, None) == ARG
+
+
+def test_fp8_math_requires_an_fp8_cache(m):
+    f = m._lib.mla_decode_partial_fp8
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    assert f(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, None) == UNSUP   # bf16 cache
+    assert f(None, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need, 0, None) == ARG
+    assert f(0x3000, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0,
+             None) == WS
