@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
                                                           const uint16_t* __restrict__ w_uv,
                                                           uint16_t* __restrict__ out, void* o_lat,
                                                           int o_bf16, float* lse_out) {
-  __shared__ __attribute__((aligned(1024))) char wt[2][CO_WBYTES];
+  __shared__ __attribute__((aligned(1024))) char wt[3][CO_WBYTES];   // W_UV chunks, two loads ahead
   __shared__ __attribute__((aligned(1024))) char at[2][CO_ABYTES];   // [hi, lo]
   const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
   const uint16_t* wsrc = w_uv + (int64_t)h * D_C * D_V;
 
   auto issue_w = [&](int kc) {
-    char* dst = wt[kc & 1] + wave * 64 * 16;
+    char* dst = wt[kc % 3] + wave * 64 * 16;
 #pragma unroll
     for (int i = 0; i < CO_KC * AQ_CHUNKS / 256; ++i) {
       const int slot = i * 256 + wave * 64 + lane;
@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
     }
   };
   issue_w(0);
+  issue_w(1);
 
   // ---- merge: thread -> row r = tid / TPR, columns 4 (tid % TPR) + 4 TPR i;
   // fewer rows in the block get more threads each (TPR = 8, 16 or 32)
@@ -289,20 +290,41 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
     const int row = ok ? (n - b * s_q) * H + h : 0;
     const int64_t sb = seg_first[b];
     const int n_split = seg_count[b];
+    // splits are taken four at a time with every load of the group in flight
+    // together (indices past the last split reload it and get weight 0), and
+    // added in split order
+    constexpr int SG = 4;
     float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, part_lse[(sb + s) * R + row]);
+    for (int s0 = 0; s0 < n_split; s0 += SG) {
+      float l[SG];
+#pragma unroll
+      for (int u = 0; u < SG; ++u) l[u] = part_lse[(sb + min(s0 + u, n_split - 1)) * R + row];
+#pragma unroll
+      for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+    }
     float wsum = 0.f;
     f32x4 acc[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s) {
-      const float ls = part_lse[(sb + s) * R + row];
-      if (ls == -INFINITY) continue;
-      const float w = exp2f(ls - mx);
-      wsum += w;
-      const float* src = part_o + ((sb + s) * R + row) * D_C + cq;
+    for (int s0 = 0; s0 < n_split; s0 += SG) {
+      float w[SG];
+      f32x4 d[SG][NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) acc[i] += w * *(const f32x4*)(src + 4 * TPR * i);
+      for (int u = 0; u < SG; ++u) {
+        const int s = min(s0 + u, n_split - 1);
+        const float ls = part_lse[(sb + s) * R + row];
+        w[u] = (s0 + u < n_split && ls != -INFINITY) ? exp2f(ls - mx) : 0.f;
+        const float* src = part_o + ((sb + s) * R + row) * D_C + cq;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) d[u][i] = *(const f32x4*)(src + 4 * TPR * i);
+      }
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        if (w[u] == 0.f) continue;      // absent or empty split: its partial may hold anything
+        wsum += w[u];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) acc[i] += w[u] * d[u][i];
+      }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     if (r >= CO_ROWS) return;
@@ -351,11 +373,18 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
   const int grp = (lane >> 4) & 1, jj = lane & 15;
   const int bcol = v0 + grp * 16 + 4 * (jj & 3);
   f32x16 acc = f32x16{};
-  for (int kc = 0; kc < D_C / CO_KC; ++kc) {
-    __builtin_amdgcn_s_waitcnt(0);
+  constexpr int NKC = D_C / CO_KC;
+  constexpr int W_LOADS = CO_KC * AQ_CHUNKS / 256;     // direct loads per thread per chunk
+  for (int kc = 0; kc < NKC; ++kc) {
+    // this thread's loads of chunk kc are done once at most those of chunk
+    // kc + 1 are outstanding (the merge's loads were consumed before)
+    if (kc + 1 < NKC)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_LOADS) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // chunk kc (and the merged operands) visible; chunk kc-1 consumed
-    if (kc + 1 < D_C / CO_KC) issue_w(kc + 1);
-    const char* w = wt[kc & 1];
+    if (kc + 2 < NKC) issue_w(kc + 2);
+    const char* w = wt[kc % 3];
 #pragma unroll
     for (int ks = 0; ks < CO_KC / 16; ++ks) {
       const int kg = kc * CO_KC + ks * 16 + half * 8;        // A columns of this lane

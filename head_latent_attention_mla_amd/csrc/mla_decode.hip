@@ -585,16 +585,35 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c4 = (threadIdx.x & 127) * 4;
   const int64_t s0 = seg_first[b];
   const int ns = seg_count[b];
+  // splits four at a time, all loads of a group in flight together; added in
+  // split order (the same order and arithmetic as combine_out_kernel's merge)
+  constexpr int SG = 4;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, part_lse[(s0 + s) * R + row]);
+  for (int g0 = 0; g0 < ns; g0 += SG) {
+    float l[SG];
+#pragma unroll
+    for (int u = 0; u < SG; ++u) l[u] = part_lse[(s0 + min(g0 + u, ns - 1)) * R + row];
+#pragma unroll
+    for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+  }
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const float ls = part_lse[(s0 + s) * R + row];
-    if (ls == -INFINITY) continue;
-    const float w = exp2f(ls - mx);
-    wsum += w;
-    acc += w * *(const f32x4*)(part_o + ((s0 + s) * R + row) * D_C + c4);
+  for (int g0 = 0; g0 < ns; g0 += SG) {
+    float w[SG];
+    f32x4 d[SG];
+#pragma unroll
+    for (int u = 0; u < SG; ++u) {
+      const int s = min(g0 + u, ns - 1);
+      const float ls = part_lse[(s0 + s) * R + row];
+      w[u] = (g0 + u < ns && ls != -INFINITY) ? exp2f(ls - mx) : 0.f;
+      d[u] = *(const f32x4*)(part_o + ((s0 + s) * R + row) * D_C + c4);
+    }
+#pragma unroll
+    for (int u = 0; u < SG; ++u) {
+      if (w[u] == 0.f) continue;
+      wsum += w[u];
+      acc += w[u] * d[u];
+    }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   acc *= inv;
