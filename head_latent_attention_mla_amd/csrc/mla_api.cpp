@@ -97,7 +97,7 @@ struct PrefillLayout {
 };
 
 // Workspace of the expand path: W_UV^T per head, then K_nope and V
-// [B, H, T_pad, 128] and the rope keys [B, T_pad, 64] (bf16), 256-aligned.
+// [B, H, T_pad, 128] (T_pad: max_seqlen rounded up to 128) and the rope keys [B, T_pad, 64] (bf16), 256-aligned.
 bool prefill_layout(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, PrefillLayout* l) {
   if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || s_q > max_seqlen) return false;
   if (B > (1 << 16) || H > (1 << 12) || max_seqlen > (1 << 24)) return false;

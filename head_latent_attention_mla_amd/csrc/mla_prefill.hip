@@ -6,10 +6,10 @@
 //
 // Two kernels:
 //   expand_kv_kernel   per (128 cached rows, head, sequence): K_nope^T and
-//       V^T tiles = W rows x C^T on MFMA (both operands straight from memory,
-//       contracted dimension contiguous), rounded to bf16 into
-//       [B, H, T_pad, 128]; the head-0 work-groups also copy the rows' rope
-//       keys to [B, T_pad, 64].  Rows past a sequence's end are written as 0.
+//       V^T tiles = W rows x C^T, an MFMA GEMM over LDS-staged chunks,
+//       rounded to bf16 into [B, H, T_pad, 128]; the head-0 work-groups also
+//       copy the rows' rope keys to [B, T_pad, 64].  Rows past a sequence's
+//       end are written as 0.
 //   prefill_attn_kernel  per (128 query rows, head, sequence): causal flash
 //       attention.  Each wave owns 32 query rows: S^T = K Q^T (the K tile from
 //       LDS, the query rows held in registers), an online softmax per row,
@@ -60,91 +60,139 @@ __device__ __forceinline__ void dequant16(u32x4 w, float s, i16x8& lo, i16x8& hi
 }
 
 // ---------------------------------------------------------------------------
-// expansion.  Wave w: output columns 64 (w & 1) .. + 63 of K_nope (w < 2) or
-// of V (w >= 2), all 128 rows of the tile: 2 column blocks x 4 row blocks of
-// 32 x 32.  D[n][t] = sum_c W[n][c] C[t][c]: A = weight rows, B = cached rows.
-// Within each 64-wide chunk of c the order is permuted alike for both
-// operands (lane half h holds c = 32 h .. 32 h + 31; MFMA j takes 8 j .. 8 j
-// + 7), so every lane reads 64 contiguous bytes.
+// expansion: one work-group per (128 cached rows, head, sequence) computes
+// D[n][t] = sum_c W[n][c] C[t][c] for the head's 256 outputs n (K_nope rows
+// of W_UK[h], then V rows of W_UV[h]^T) -- a GEMM with K = 512 in 8 chunks of
+// 64.  Each chunk of the cached rows (128 x 128 B) and of the weight rows
+// (256 x 128 B) is staged in LDS (direct loads for bf16 rows; e4m3 rows are
+// dequantised through registers), double-buffered, with the 16-byte chunk
+// index XOR row & 7 so the fragment reads are conflict-free.  Wave w owns
+// outputs 64 w .. 64 w + 63 for all 128 rows: 2 x 4 blocks of 32 x 32.
 // ---------------------------------------------------------------------------
+constexpr int EC = 64;                          // contracted values per chunk
+constexpr int E_ROWB = EC * 2;                  // 128 B per staged row
+constexpr int E_CT = ET * E_ROWB;               // 16 KB: the cached rows of one chunk
+constexpr int E_WT = 256 * E_ROWB;              // 32 KB: the weight rows of one chunk
+static_assert(ET == 128, "expansion tile");
+
 __global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char cbuf[2][E_CT];
+  __shared__ __attribute__((aligned(1024))) char wbuf[2][E_WT];
   const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int T = p.seqlens[b];
   const int t0 = tt * ET;
-  const bool is_v = wave >= 2;
-  const uint16_t* W = (is_v ? p.w_uvt : p.w_uk) + (int64_t)h * D_NOPE * D_C;
-  const int n0 = 64 * (wave & 1);
+  const uint32_t cbuf_a = lds_addr(cbuf), wbuf_a = lds_addr(wbuf);
 
-  // cached rows of this lane for the 4 row blocks (clamped into the sequence:
-  // rows past its end are computed from a real row and stored as zeros)
-  int64_t crow[4];
-  float csc[4];
+  // staging geometry: 1 KB load L fills rows 8 L + lane / 8, slot lane % 8,
+  // which holds logical chunk (lane % 8) ^ (row & 7).  Wave w issues cached
+  // loads 4 w .. 4 w + 3 (rows 32 w + 8 i + lane / 8) and weight loads
+  // 8 w .. 8 w + 7 (rows 64 w + 8 i + lane / 8)
+  const int sch = (lane & 7) ^ ((lane >> 3) & 7);
+  int32_t crow[4];                                     // cache row index of each staged row
+  float cscale[4];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int t = min(t0 + 32 * rb + l32, T - 1);
-    crow[rb] = cache_row(p, b, t);
-    csc[rb] = p.fp8 ? p.row_scale[crow[rb]] : 1.0f;
+  for (int i = 0; i < 4; ++i) {
+    const int t = min(t0 + 32 * wave + 8 * i + (lane >> 3), T - 1);   // rows past the end reuse a real row
+    const int64_t cr = cache_row(p, b, t);
+    crow[i] = (int32_t)cr;
+    cscale[i] = p.fp8 ? p.row_scale[cr] : 1.0f;
   }
-  const uint16_t* wr0 = W + (int64_t)(n0 + l32) * D_C + 32 * half;
-  const uint16_t* wr1 = W + (int64_t)(n0 + 32 + l32) * D_C + 32 * half;
+  // weight rows 64 w + 8 i + lane / 8: W_UK[h] rows for waves 0, 1, W_UV[h]^T rows for 2, 3
+  const uint16_t* wbase = (wave < 2 ? p.w_uk : p.w_uvt) +
+                          ((int64_t)h * D_NOPE + ((64 * wave) & 127) + (lane >> 3)) * D_C + 8 * sch;
+  const int elem = p.fp8 ? 1 : 2;
+
+  // a chunk's loads are issued right after the barrier that frees its buffer;
+  // e4m3 rows arrive in registers and are dequantised into LDS after the
+  // current chunk's products
+  uint64_t c8[4];
+  auto stage_issue = [&](int ch, int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(wbase + 8 * i * D_C + ch * EC),
+                                       (lds_void_t*)(wbuf[buf] + (8 * wave + i) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* src = (const char*)p.rows + ((int64_t)crow[i] * ROWW + ch * EC + 8 * sch) * elem;
+      if (p.fp8)
+        c8[i] = *(const uint64_t*)src;
+      else
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(cbuf[buf] + (4 * wave + i) * 1024), 16,
+                                         0, 0);
+    }
+  };
+  auto stage_finish = [&](int buf) {
+    if (!p.fp8) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      i16x8 lo, hi;
+      const u32x4 wv = {(uint32_t)c8[i], (uint32_t)(c8[i] >> 32), 0u, 0u};
+      dequant16(wv, cscale[i], lo, hi);
+      (void)hi;
+      *(i16x8*)(cbuf[buf] + (4 * wave + i) * 1024 + lane * 16) = lo;
+    }
+  };
+
+  // fragment reads: row r of a staged tile, logical chunk 2 ks + half
+  uint32_t fo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) fo[ks] = l32 * E_ROWB + 16 * ((2 * ks + half) ^ (l32 & 7));
+  const uint32_t arow = (uint32_t)(64 * wave) * E_ROWB;   // this wave's weight rows
 
   f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int k = 0; k < 4; ++k) acc[i][k] = f32x16{};
 
-  for (int ch = 0; ch < D_C / 64; ++ch) {
-    i16x8 a[2][4], bb[4][4];
+  stage_issue(0, 0);
+  stage_finish(0);
+  for (int ch = 0; ch < D_C / EC; ++ch) {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // chunk ch staged; other buffer free
+    if (ch + 1 < D_C / EC) stage_issue(ch + 1, (ch + 1) & 1);
+    const uint32_t wa = wbuf_a + (ch & 1) * E_WT + arow;
+    const uint32_t ca = cbuf_a + (ch & 1) * E_CT;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a[0][j] = ld16(wr0 + ch * 64 + 8 * j);
-      a[1][j] = ld16(wr1 + ch * 64 + 8 * j);
+    for (int ks = 0; ks < 4; ++ks) {
+      i16x8 af[2], bf[4];
+      static_for<0, 2>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_read_b128<i * 32 * E_ROWB>(af[i], wa + fo[ks]);
+      });
+      static_for<0, 4>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        lds_read_b128<i * 32 * E_ROWB>(bf[i], ca + fo[ks]);
+      });
+      wait_lgkm<0>(af[0], af[1], bf[0], bf[1], bf[2], bf[3]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[nb][tb] = mfma32(__builtin_bit_cast(bf16x8, af[nb]), __builtin_bit_cast(bf16x8, bf[tb]), acc[nb][tb]);
     }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if (p.fp8) {
-        const uint8_t* src = (const uint8_t*)p.rows + crow[rb] * ROWW + ch * 64 + 32 * half;
-        const u32x4 w0 = *(const u32x4*)src;
-        const u32x4 w1 = *(const u32x4*)(src + 16);
-        dequant16(w0, csc[rb], bb[rb][0], bb[rb][1]);
-        dequant16(w1, csc[rb], bb[rb][2], bb[rb][3]);
-      } else {
-        const uint16_t* src = (const uint16_t*)p.rows + crow[rb] * ROWW + ch * 64 + 32 * half;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bb[rb][j] = ld16(src + 8 * j);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          acc[cb][rb] = mfma32(__builtin_bit_cast(bf16x8, a[cb][j]), __builtin_bit_cast(bf16x8, bb[rb][j]),
-                               acc[cb][rb]);
+    if (ch + 1 < D_C / EC) stage_finish((ch + 1) & 1);
   }
 
-  // lane holds D[n = 32 cb + 8 g + 4 half + e][t = 32 rb + l32], e < 4: four
-  // consecutive outputs of one row, stored as 8 bytes
-  uint16_t* dst = (is_v ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE;
+  // lane holds D[n = 64 w + 32 nb + 8 g + 4 half + e][t = 32 tb + l32], e < 4:
+  // four consecutive outputs of one row, stored as 8 bytes
+  uint16_t* dst = (wave >= 2 ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE + (64 * wave) % 128;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int t = 32 * rb + l32;
+  for (int tb = 0; tb < 4; ++tb) {
+    const int t = 32 * tb + l32;
     const bool live = t0 + t < T;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint64_t v = 0;
         if (live) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[cb][rb][4 * g + e])) << (16 * e);
+          for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[nb][tb][4 * g + e])) << (16 * e);
         }
-        *(uint64_t*)(dst + (int64_t)t * D_NOPE + n0 + 32 * cb + 8 * g + 4 * half) = v;
+        *(uint64_t*)(dst + (int64_t)t * D_NOPE + 32 * nb + 8 * g + 4 * half) = v;
       }
   }
 
