@@ -5,11 +5,11 @@
 // K = C W_UK and V = C W_UV once, then run ordinary attention over them).
 //
 // Two kernels:
-//   expand_kv_kernel   per (128 cached rows, head, sequence): K_nope^T and
-//       V^T tiles = W rows x C^T, an MFMA GEMM over LDS-staged chunks,
-//       rounded to bf16 into [B, H, T_pad, 128]; the head-0 work-groups also
-//       copy the rows' rope keys to [B, T_pad, 64].  Rows past a sequence's
-//       end are written as 0.
+//   expand_kv_kernel   one persistent work-group per (head, K or V) holds that
+//       half of the head's weights in LDS and streams every cached row
+//       through MFMA: K_nope^T and V^T tiles rounded to bf16 into
+//       [B, H, T_pad, 128] (rows past a sequence's end written as 0);
+//       copy_rope_kernel copies the rows' rope keys to [B, T_pad, 64].
 //   prefill_attn_kernel  per (128 query rows, head, sequence): causal flash
 //       attention.  Each wave owns 32 query rows: S^T = K Q^T (the K tile from
 //       LDS, the query rows held in registers), an online softmax per row,
@@ -60,167 +60,178 @@ __device__ __forceinline__ void dequant16(u32x4 w, float s, i16x8& lo, i16x8& hi
 }
 
 // ---------------------------------------------------------------------------
-// expansion: one work-group per (128 cached rows, head, sequence) computes
-// D[n][t] = sum_c W[n][c] C[t][c] for the head's 256 outputs n (K_nope rows
-// of W_UK[h], then V rows of W_UV[h]^T) -- a GEMM with K = 512 in 8 chunks of
-// 64.  Each chunk of the cached rows (128 x 128 B) and of the weight rows
-// (256 x 128 B) is staged in LDS (direct loads for bf16 rows; e4m3 rows are
-// dequantised through registers), double-buffered, with the 16-byte chunk
-// index XOR row & 7 so the fragment reads are conflict-free.  Wave w owns
-// outputs 64 w .. 64 w + 63 for all 128 rows: 2 x 4 blocks of 32 x 32.
+// expansion: one persistent work-group per (head, K or V) keeps that half of
+// the head's weights -- W_UK[h] or W_UV[h]^T, 128 rows x 512 -- in LDS (128
+// KB, 16-byte chunks XOR row & 7) and walks every 128-row tile of every
+// sequence: D[n][t] = sum_c W[n][c] C[t][c], K = 512 in 8 chunks of 64.  Wave
+// (nq, tq) = (w & 1, w >> 1) owns outputs 64 nq .. + 63 and tile rows 64 tq ..
+// + 63 (2 x 2 blocks of 32 x 32).  The cached-row fragments go straight to
+// registers, three chunks ahead across tile boundaries; within a chunk the k
+// order is permuted alike for both operands (lane half h holds c = 32 h ..
+// 32 h + 31, MFMA j takes 8 j .. 8 j + 7), so a lane reads 64 contiguous bytes.
 // ---------------------------------------------------------------------------
-constexpr int EC = 64;                          // contracted values per chunk
-constexpr int E_ROWB = EC * 2;                  // 128 B per staged row
-constexpr int E_CT = ET * E_ROWB;               // 16 KB: the cached rows of one chunk
-constexpr int E_WT = 256 * E_ROWB;              // 32 KB: the weight rows of one chunk
-static_assert(ET == 128, "expansion tile");
+constexpr int E_AHEAD = 3;                      // chunks of cached-row fragments in flight
+constexpr int E_NCH = D_C / 64;                 // 8 chunks of 64 per tile
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char cbuf[2][E_CT];
-  __shared__ __attribute__((aligned(1024))) char wbuf[2][E_WT];
-  const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  __shared__ __attribute__((aligned(1024))) char wl[D_NOPE * D_C * 2];   // 128 KB
+  const int h = blockIdx.x >> 1, part = blockIdx.x & 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
+  const int nq = wave & 1, tq = wave >> 1;
+  const uint32_t wl_a = lds_addr(wl);
+
+  // the weight half: row L of 1 KB is load L (wave w: rows 32 w .. + 31);
+  // slot lane holds logical chunk lane ^ (L & 7)
+  {
+    const uint16_t* W = (part ? p.w_uvt : p.w_uk) + (int64_t)h * D_NOPE * D_C;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int L = 32 * wave + i;
+      __builtin_amdgcn_global_load_lds((const void*)(W + (int64_t)L * D_C + 8 * (lane ^ (L & 7))),
+                                       (lds_void_t*)(wl + L * 1024), 16, 0, 0);
+    }
+  }
+  // A-fragment reads: row 64 nq + 32 nb + l32, logical chunk 8 ch + 4 half + j
+  uint32_t wo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wo[j] = wl_a + (64 * nq + l32) * 1024 + 16 * ((4 * half + j) ^ (l32 & 7));
+
+  const int n_tt = p.T_pad / ET;
+  const int n_steps = p.B * n_tt * E_NCH;
+  constexpr int elem = FP8 ? 1 : 2;
+  // the cached row behind fragment (step s, t-block tb) of this lane; rows
+  // past a sequence's end reuse its last row (their outputs are stored as 0)
+  auto frag_src = [&](int s, int tb, float& sc) -> const char* {
+    const int tile = s / E_NCH, ch = s % E_NCH;
+    const int b = tile / n_tt, tt = tile % n_tt;
+    const int T = p.seqlens[b];
+    const int t = min(tt * ET + 64 * tq + 32 * tb + l32, T - 1);
+    const int64_t r = cache_row(p, b, t);
+    sc = FP8 ? p.row_scale[r] : 1.0f;
+    return (const char*)p.rows + (r * ROWW + ch * 64 + 32 * half) * elem;
+  };
+  // ring of fragments (bf16 rows) or raw codes and scales (e4m3 rows)
+  i16x8 cf[E_AHEAD + 1][2][FP8 ? 1 : 4];
+  float csc[E_AHEAD + 1][2];
+  uint32_t c8[E_AHEAD + 1][2][FP8 ? 8 : 1];
+  auto issue = [&](int s, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const char* src = frag_src(s, tb, csc[slot][tb]);
+      if constexpr (FP8) {
+        const u32x4 a = *(const u32x4*)src, c = *(const u32x4*)(src + 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          c8[slot][tb][q] = a[q];
+          c8[slot][tb][4 + q] = c[q];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cf[slot][tb][j] = *(const i16x8*)(src + 16 * j);
+      }
+    }
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();                                     // the weights are in LDS
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
+  // the step loop is unrolled by the ring size so every ring slot is a
+  // compile-time index
+  static_for<0, E_AHEAD>([&](auto sc) {
+    if (decltype(sc)::value < n_steps) issue(decltype(sc)::value, sc);
+  });
+  for (int s0 = 0; s0 < n_steps; s0 += E_AHEAD + 1) {
+    static_for<0, E_AHEAD + 1>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      const int s = s0 + u;
+      if (s >= n_steps) return;
+      if (s + E_AHEAD < n_steps) issue(s + E_AHEAD, std::integral_constant<int, (u + E_AHEAD) % (E_AHEAD + 1)>{});
+      const int tile = s / E_NCH, ch = s % E_NCH;
+      i16x8 bf[2][4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        if constexpr (FP8) {
+          dequant16(u32x4{c8[u][tb][0], c8[u][tb][1], c8[u][tb][2], c8[u][tb][3]}, csc[u][tb], bf[tb][0], bf[tb][1]);
+          dequant16(u32x4{c8[u][tb][4], c8[u][tb][5], c8[u][tb][6], c8[u][tb][7]}, csc[u][tb], bf[tb][2], bf[tb][3]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bf[tb][j] = cf[u][tb][j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        i16x8 af[2];
+        const uint32_t a = wo[j] + ch * 128;
+        lds_read_b128<0>(af[0], a);
+        lds_read_b128<32 * 1024>(af[1], a);
+        wait_lgkm<0>(af[0], af[1]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            acc[nb][tb] = mfma32(__builtin_bit_cast(bf16x8, af[nb]), __builtin_bit_cast(bf16x8, bf[tb][j]), acc[nb][tb]);
+      }
+      if (ch == E_NCH - 1) {
+        // lane holds D[n = 64 nq + 32 nb + 8 g + 4 half + e][t = 64 tq + 32 tb + l32]
+        const int b = tile / n_tt, t0 = (tile % n_tt) * ET;
+        const int T = p.seqlens[b];
+        uint16_t* dst = (part ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const int t = 64 * tq + 32 * tb + l32;
+          const bool live = t0 + t < T;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              uint64_t v = 0;
+              if (live) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[nb][tb][4 * g + e])) << (16 * e);
+              }
+              *(uint64_t*)(dst + (int64_t)t * D_NOPE + 64 * nq + 32 * nb + 8 * g + 4 * half) = v;
+            }
+            acc[nb][tb] = f32x16{};
+          }
+        }
+      }
+    });
+  }
+}
+
+// the rope keys of every row: [B, T_pad, 64] bf16 (zeros past a sequence's end)
+__global__ __launch_bounds__(256) void copy_rope_kernel(PrefillParams p) {
+  const int tt = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int T = p.seqlens[b];
   const int t0 = tt * ET;
-  const uint32_t cbuf_a = lds_addr(cbuf), wbuf_a = lds_addr(wbuf);
-
-  // staging geometry: 1 KB load L fills rows 8 L + lane / 8, slot lane % 8,
-  // which holds logical chunk (lane % 8) ^ (row & 7).  Wave w issues cached
-  // loads 4 w .. 4 w + 3 (rows 32 w + 8 i + lane / 8) and weight loads
-  // 8 w .. 8 w + 7 (rows 64 w + 8 i + lane / 8)
-  const int sch = (lane & 7) ^ ((lane >> 3) & 7);
-  int32_t crow[4];                                     // cache row index of each staged row
-  float cscale[4];
+  uint16_t* rdst = p.rope + ((int64_t)b * p.T_pad + t0) * D_ROPE;
+  if (p.fp8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = min(t0 + 32 * wave + 8 * i + (lane >> 3), T - 1);   // rows past the end reuse a real row
-    const int64_t cr = cache_row(p, b, t);
-    crow[i] = (int32_t)cr;
-    cscale[i] = p.fp8 ? p.row_scale[cr] : 1.0f;
-  }
-  // weight rows 64 w + 8 i + lane / 8: W_UK[h] rows for waves 0, 1, W_UV[h]^T rows for 2, 3
-  const uint16_t* wbase = (wave < 2 ? p.w_uk : p.w_uvt) +
-                          ((int64_t)h * D_NOPE + ((64 * wave) & 127) + (lane >> 3)) * D_C + 8 * sch;
-  const int elem = p.fp8 ? 1 : 2;
-
-  // a chunk's loads are issued right after the barrier that frees its buffer;
-  // e4m3 rows arrive in registers and are dequantised into LDS after the
-  // current chunk's products
-  uint64_t c8[4];
-  auto stage_issue = [&](int ch, int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(wbase + 8 * i * D_C + ch * EC),
-                                       (lds_void_t*)(wbuf[buf] + (8 * wave + i) * 1024), 16, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i;            // row idx / 4, codes 16 (idx % 4) .. + 15
+      const int t = idx >> 2, qd = idx & 3;
+      i16x8 lo = {0, 0, 0, 0, 0, 0, 0, 0}, hi = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t0 + t < T) {
+        const int64_t r = cache_row(p, b, t0 + t);
+        dequant16(*(const u32x4*)((const uint8_t*)p.rows + r * ROWW + D_C + 16 * qd), p.row_scale[r], lo, hi);
+      }
+      *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd) = lo;
+      *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd + 8) = hi;
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const char* src = (const char*)p.rows + ((int64_t)crow[i] * ROWW + ch * EC + 8 * sch) * elem;
-      if (p.fp8)
-        c8[i] = *(const uint64_t*)src;
-      else
-        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)(cbuf[buf] + (4 * wave + i) * 1024), 16,
-                                         0, 0);
-    }
-  };
-  auto stage_finish = [&](int buf) {
-    if (!p.fp8) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      i16x8 lo, hi;
-      const u32x4 wv = {(uint32_t)c8[i], (uint32_t)(c8[i] >> 32), 0u, 0u};
-      dequant16(wv, cscale[i], lo, hi);
-      (void)hi;
-      *(i16x8*)(cbuf[buf] + (4 * wave + i) * 1024 + lane * 16) = lo;
-    }
-  };
-
-  // fragment reads: row r of a staged tile, logical chunk 2 ks + half
-  uint32_t fo[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) fo[ks] = l32 * E_ROWB + 16 * ((2 * ks + half) ^ (l32 & 7));
-  const uint32_t arow = (uint32_t)(64 * wave) * E_ROWB;   // this wave's weight rows
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc[i][k] = f32x16{};
-
-  stage_issue(0, 0);
-  stage_finish(0);
-  for (int ch = 0; ch < D_C / EC; ++ch) {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");   // chunk ch staged; other buffer free
-    if (ch + 1 < D_C / EC) stage_issue(ch + 1, (ch + 1) & 1);
-    const uint32_t wa = wbuf_a + (ch & 1) * E_WT + arow;
-    const uint32_t ca = cbuf_a + (ch & 1) * E_CT;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      i16x8 af[2], bf[4];
-      static_for<0, 2>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        lds_read_b128<i * 32 * E_ROWB>(af[i], wa + fo[ks]);
-      });
-      static_for<0, 4>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        lds_read_b128<i * 32 * E_ROWB>(bf[i], ca + fo[ks]);
-      });
-      wait_lgkm<0>(af[0], af[1], bf[0], bf[1], bf[2], bf[3]);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          acc[nb][tb] = mfma32(__builtin_bit_cast(bf16x8, af[nb]), __builtin_bit_cast(bf16x8, bf[tb]), acc[nb][tb]);
-    }
-    if (ch + 1 < D_C / EC) stage_finish((ch + 1) & 1);
-  }
-
-  // lane holds D[n = 64 w + 32 nb + 8 g + 4 half + e][t = 32 tb + l32], e < 4:
-  // four consecutive outputs of one row, stored as 8 bytes
-  uint16_t* dst = (wave >= 2 ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE + (64 * wave) % 128;
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    const int t = 32 * tb + l32;
-    const bool live = t0 + t < T;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint64_t v = 0;
-        if (live) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[nb][tb][4 * g + e])) << (16 * e);
-        }
-        *(uint64_t*)(dst + (int64_t)t * D_NOPE + 32 * nb + 8 * g + 4 * half) = v;
-      }
-  }
-
-  // rope keys of the tile's rows (head-0 work-groups): 128 rows x 64 values
-  if (h == 0) {
-    uint16_t* rdst = p.rope + ((int64_t)b * p.T_pad + t0) * D_ROPE;
-    if (p.fp8) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int idx = tid + 256 * i;            // row idx / 4, codes 16 (idx % 4) .. + 15
-        const int t = idx >> 2, qd = idx & 3;
-        i16x8 lo = {0, 0, 0, 0, 0, 0, 0, 0}, hi = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t0 + t < T) {
-          const int64_t r = cache_row(p, b, t0 + t);
-          dequant16(*(const u32x4*)((const uint8_t*)p.rows + r * ROWW + D_C + 16 * qd), p.row_scale[r], lo, hi);
-        }
-        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd) = lo;
-        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 16 * qd + 8) = hi;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;            // row idx / 8, values 8 (idx % 8) .. + 7
-        const int t = idx >> 3, c = idx & 7;
-        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (t0 + t < T) v = ld16((const uint16_t*)p.rows + cache_row(p, b, t0 + t) * ROWW + D_C + 8 * c);
-        *(i16x8*)(rdst + (int64_t)t * D_ROPE + 8 * c) = v;
-      }
+      const int idx = tid + 256 * i;            // row idx / 8, values 8 (idx % 8) .. + 7
+      const int t = idx >> 3, c = idx & 7;
+      i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t0 + t < T) v = ld16((const uint16_t*)p.rows + cache_row(p, b, t0 + t) * ROWW + D_C + 8 * c);
+      *(i16x8*)(rdst + (int64_t)t * D_ROPE + 8 * c) = v;
     }
   }
 }
@@ -474,7 +485,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(expand_kv_kernel, dim3(p.T_pad / ET, p.H, p.B), dim3(256), 0, stream, p);
+  if (p.fp8)
+    hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(expand_kv_kernel<false>, dim3(2 * p.H), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(copy_rope_kernel, dim3(p.T_pad / ET, p.B), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_qt = (p.s_q + QT - 1) / QT;
