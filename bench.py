@@ -459,7 +459,10 @@ def main():
 
     # per-kernel durations with HIP events on the launch stream (recorded
     # back to back, read after one synchronisation)
-    names = ["absorb_q", "sparse_gather+decode_split" if sparse else "decode_split", "combine_out"]
+    fused_gather = sparse and not cache0.paged and not cache0.fp8
+    scan_name = ("decode_split (gather fused)" if fused_gather else "sparse_gather+decode_split") if sparse \
+        else "decode_split"
+    names = ["absorb_q", scan_name, "combine_out"]
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
@@ -485,7 +488,8 @@ def main():
     # more query tokens per cached row or an fp8 cache push it past (MFMA-bound)
     hbm_bound = (not fp8) and s_q == 1
     roofline = {
-        "kernel": ("sparse gather + split-T scan (selected rows counted once)" if sparse
+        "kernel": ("split-T scan gathering the selected rows (counted once)" if fused_gather
+                   else "sparse gather + split-T scan (selected rows counted once)" if sparse
                    else "decode_split_f8 (split-T latent scan, E4M3 arithmetic)" if f8m
                    else "decode_split (split-T latent scan)"),
         "bound": "hbm" if hbm_bound else "mfma",

@@ -200,9 +200,13 @@ int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H, int32_t max_seq
 
 namespace {
 
+// sel_idx != null: sparse top-k with the gather fused into the scan's loader
+// (contiguous bf16 caches only); sel_count / k_max replace the lengths
 mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                                int32_t H, float softmax_scale, int32_t causal, void* workspace,
-                               size_t ws_bytes, int32_t num_splits, hipStream_t st, bool fp8_math = false) {
+                               size_t ws_bytes, int32_t num_splits, hipStream_t st, bool fp8_math = false,
+                               const int32_t* sel_idx = nullptr, const int32_t* sel_count = nullptr,
+                               int32_t k_max = 0) {
   if (q_lat == nullptr) return MLA_ERR_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || num_splits < 0) return MLA_ERR_ARG;
   if (causal != 0 && causal != 1) return MLA_ERR_ARG;
@@ -210,7 +214,8 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   const mla_status ks = check_kv(kv, s_q);
   if (ks != MLA_OK) return ks;
   Plan pl;
-  if (!make_plan(B, s_q, H, kv->max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
+  const int32_t plan_len = sel_idx != nullptr ? k_max : kv->max_seqlen;
+  if (!make_plan(B, s_q, H, plan_len, num_splits, &pl)) return MLA_ERR_ARG;
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
 
   mla::DecodeParams p{};
@@ -237,6 +242,12 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   p.causal = causal;
   p.paged = kv->block_table != nullptr;
   p.fp8 = kv->dtype == MLA_FP8_E4M3;
+  if (sel_idx != nullptr) {
+    p.seqlens = sel_count;
+    p.src_len = kv->seqlens;
+    p.sel_idx = sel_idx;
+    p.k_max = k_max;
+  }
   if (fp8_math) {
     if (!p.fp8) return MLA_ERR_UNSUPPORTED;
     return hip_status(mla::launch_decode_split_f8(p, st));
@@ -358,6 +369,11 @@ mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv, c
     return MLA_ERR_ARG;
   if (workspace == nullptr || ws_bytes < total) return MLA_ERR_WORKSPACE;
   const bool fp8 = kv->dtype == MLA_FP8_E4M3;
+  // contiguous bf16 caches whose sequences fit the loader's 32-bit window:
+  // the scan gathers the selected rows itself
+  if (kv->block_table == nullptr && !fp8 && (int64_t)kv->T_stride * mla::ROWW * 2 <= ((int64_t)1 << 30))
+    return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, 0, workspace, pl.ws_bytes, num_splits,
+                               (hipStream_t)stream, false, sel_idx, sel_count, k_max);
   mla::GatherParams g{};
   g.rows = kv->rows;
   g.row_scale = kv->row_scale;

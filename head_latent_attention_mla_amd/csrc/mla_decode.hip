@@ -84,7 +84,11 @@ __device__ __forceinline__ int opaque(int x) {
 constexpr int STAGE_BYTES = KT * ROWW;        // 36,864: e4m3 codes of one tile
 static_assert(TILE_BYTES + 2 * STAGE_BYTES == 2 * TILE_BYTES, "layouts share the P offset");
 
-template <bool PAGED, bool FP8>
+// SPARSE (contiguous bf16 caches): the tile rows are the selected positions
+// sel_idx[b, ts ..] of sequence b instead of rows ts.. -- the gather of sparse
+// top-k decode fused into the tile loader; p.seqlens holds the selection
+// counts (clamped here to [0, k_max]) and p.src_len the cache lengths.
+template <bool PAGED, bool FP8, bool SPARSE = false>
 __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * TILE_BYTES + P_BYTES];
   char* const pbuf = smem + 2 * TILE_BYTES;
@@ -112,6 +116,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   int b, j, parts;
   int sl;
   int g;
+  auto seq_len = [&](int bb) -> int {
+    if constexpr (SPARSE) return min(max(p.seqlens[bb], 0), p.k_max);
+    return p.seqlens[bb];
+  };
   {
     int64_t* scan = (int64_t*)pbuf;        // 2 x 256 entries; the probability buffer is idle here
     int64_t* found = scan + 2 * NTHREADS;  // the slot's sequence and its first slot
@@ -136,13 +144,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       return v + before;
     };
     int64_t tiles_mine = 0;
-    for (int bb = c0; bb < c1; ++bb) tiles_mine += (p.seqlens[bb] + KT - 1) / KT;
+    for (int bb = c0; bb < c1; ++bb) tiles_mine += (seq_len(bb) + KT - 1) / KT;
     (void)inclusive_scan(tiles_mine);
     const int64_t total = uniform64(found[2]);
     // in [1, max(n_t, 1)]: every part holds a tile, and a sequence without
     // rows still gets one (empty) part, whose partial merges to zero
     auto parts_of = [&](int bb) -> int {
-      const int64_t nt = (p.seqlens[bb] + KT - 1) / KT;
+      const int64_t nt = (seq_len(bb) + KT - 1) / KT;
       if (total == 0 || nt == 0) return 1;
       const int64_t q = floor_div(nt * p.n_ranges, total);
       return (int)(q < 1 ? 1 : (q > nt ? nt : q));
@@ -178,8 +186,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       p.seg_count[b] = parts;
     }
   }
-  const int nt_b = (p.seqlens[b] + KT - 1) / KT;
-  const int T = p.seqlens[b];
+  const int nt_b = (seq_len(b) + KT - 1) / KT;
+  const int T = seq_len(b);
   const int t_begin = (int)floor_div((int64_t)j * nt_b, parts) * KT;
   const int t_end = min(T, (int)floor_div((int64_t)(j + 1) * nt_b, parts) * KT);
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + KT - 1) / KT : 0;
@@ -227,10 +235,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   };
   // live = false gives an empty window: its loads fetch nothing and write zeros
   auto tile_rsrc = [&](int tile, bool live) {
+    if constexpr (SPARSE) {
+      // the whole sequence: a selected position outside it reads as a zero row
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + (int64_t)b * p.T_stride * ROWW * ELEM), (short)0,
+                                               live ? p.src_len[b] * ROWW * ELEM : 0, 0x00020000);
+    }
     const int ts = t_begin + tile * KT;
     const int valid = live ? min(KT, T - ts) : 0;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW * ELEM), (short)0,
                                              valid * ROWW * ELEM, 0x00020000);
+  };
+  // SPARSE: row offsets of this wave's 16 tile rows, relative to the loader's
+  // 8-row pattern (adj[r] + the pattern offset = position * 1152 + chunk);
+  // rows past the selection or outside the sequence point past the window
+  constexpr uint32_t OOB = 0x40000000u;
+  uint32_t adj[16];
+  auto set_rows = [&](int tile) {
+    if constexpr (SPARSE) {
+      const int r0 = t_begin + tile * KT + 16 * wave;
+      const int32_t* ip = p.sel_idx + (int64_t)b * p.k_max + r0;
+      const int src = p.src_len[b];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pos = r0 + r < T ? ip[r] : -1;
+        const uint32_t a = (pos >= 0 && pos < src) ? (uint32_t)(pos - (r & 7)) * (ROWW * 2) : OOB;
+        adj[r] = __builtin_amdgcn_readfirstlane(a);
+      }
+    }
   };
   const int soff = wave * (16 * ROWW * ELEM);
   auto issue_load = [&](__amdgpu_buffer_rsrc_t rsrc, int buf, auto kc) {
@@ -243,8 +274,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       constexpr int k9 = k % 9;
       const uint32_t vo = (loff[k9 >> 1] >> (16 * (k9 & 1))) & 0xFFFFu;
       char* dst = smem + buf * TILE_BYTES + wave * (16 * ROWW * 2) + k * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
-                                               soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+      if constexpr (SPARSE) {
+        // load k covers pattern rows a and a + 1 (lanes from `split` on)
+        constexpr int a = (64 * k9) / CHUNKS;
+        constexpr int split = CHUNKS * (a + 1) - 64 * k9;
+        constexpr int r = a + (k >= 9 ? 8 : 0);
+        uint32_t row_adj = adj[r];
+        if constexpr (split < 64) row_adj = lane < split ? adj[r] : adj[r + 1];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo + row_adj, 0, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
+                                                 soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+      }
     }
   };
   constexpr int NLOADS = FP8 ? 9 : 18;         // 1 KB loads per wave per tile
@@ -323,6 +364,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 
   float sc_cur = 0.f, sc_next = 0.f;            // FP8 row scales (this tile, next)
   if (n_tiles > 0) {
+    set_rows(0);
     issue_tile(0, 0);
     if constexpr (FP8) sc_next = load_scale(0);
   }
@@ -333,6 +375,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     // past the last tile the loads still run (no branch in the loop) but
     // read an empty window into the idle buffer
     const auto next = tile_rsrc(has_next ? tile + 1 : tile, has_next);
+    if constexpr (SPARSE) set_rows(has_next ? tile + 1 : tile);
     const int next_buf = (tile + 1) & 1;
     uint32_t tb_a;
     if constexpr (FP8) {
@@ -634,6 +677,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream) {
   const int grid = 8 * p.work_per_xcd;
+  if (p.sel_idx != nullptr) {
+    hipLaunchKernelGGL((decode_split_kernel<false, false, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.paged) {
     if (p.fp8)
       hipLaunchKernelGGL((decode_split_kernel<true, true>), dim3(grid), dim3(NTHREADS), 0, stream, p);

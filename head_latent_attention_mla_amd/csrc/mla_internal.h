@@ -37,6 +37,11 @@ struct DecodeParams {
   int32_t causal;
   int32_t paged;
   int32_t fp8;
+  // sparse top-k with the gather fused into the loader (contiguous bf16
+  // caches): seqlens then holds the selection counts
+  const int32_t* sel_idx;       // [B, k_max] selected positions, or null
+  const int32_t* src_len;       // [B] cache lengths
+  int32_t k_max;
 };
 
 // One call of the naive (expand-then-attend) ablation.

@@ -246,8 +246,10 @@ mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int3
  * selected row gets zeros.  For query token j, head h:
  *   o_lat[b,j,h,:] = sum_{i < sel_count[b]} softmax_i(scale * <q_lat[b,j,h,:],
  *                    row_{sel_idx[b,i]}>) * row_{sel_idx[b,i]}[0:512]
- * Steps: the selected rows are gathered into a compact cache inside the
- * workspace, which the split-T scan of mla_decode_partial reads.
+ * Steps: for a contiguous bf16 cache (T_stride * 1152 <= 2^30) the split-T
+ * scan loads the selected rows itself; otherwise (paged or e4m3 caches) they
+ * are first gathered into a compact cache inside the workspace, which the
+ * scan then reads.
  *   kv         the full cache (contiguous or paged, bf16 or e4m3)
  *   sel_idx    int32 [B, k_max]; sel_count int32 [B], each <= k_max
  *   k_max      row stride of sel_idx and the largest selection (>= s_q)

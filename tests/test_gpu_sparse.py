@@ -95,3 +95,25 @@ def test_sparse_full_size_sampled(mla):
     ref = O.sparse_decode(inp, sel, cnt, SCALE, pairs=pairs)
     for b, h in pairs:
         _assert_close(got[b, :, h], ref[b, :, h], what=f"sparse full ({b},{h})")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_out_of_range_positions_read_zero_rows(mla, paged):
+    """A selected position outside [0, T_b) contributes a zero row (score 0,
+    value 0), in the fused loader (contiguous bf16) and in the gather path
+    (paged): the expectation is the oracle on a copy of the cache with one
+    extra zero row that those entries point at."""
+    w = W.Workload("sp_oob", B=2, H=64, s_q=1, causal=False, T=200, paged=paged, seed=86)
+    inp = W.generate(w)
+    sel = np.full((2, 40), -1, dtype=np.int32)
+    sel[0, :6] = [5, -3, 199, 200, 7, 100000]
+    sel[1, :4] = [0, 1, -1, 150]
+    cnt = np.array([6, 4], dtype=np.int32)
+    got = _f64(_run(mla, inp, sel, cnt))
+    # expected: the same selection on contiguous rows plus a zero row at T
+    cont = W.as_contiguous(inp)
+    rows = np.concatenate([cont["rows"], np.zeros((2, 1, 576), dtype=cont["rows"].dtype)], axis=1)
+    ref_inp = dict(cont, rows=rows, seqlens=cont["seqlens"] + 1)
+    fixed = np.where((sel >= 0) & (sel < 200), sel, 200).astype(np.int32)
+    ref = O.sparse_decode(ref_inp, fixed, cnt, SCALE)
+    _assert_close(got, ref, what=f"out of range (paged={paged})")
