@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 N_COPIES = 3
+PART_DTYPE_NAME = "bf16"     # split partials of the decode step: half the fp32 partial traffic
 
 
 def algorithmic_counts(B, s_q, H, seqlens, causal, cache_elem_bytes=2, scale_bytes=0):
@@ -428,6 +429,8 @@ def main():
         ws = torch.empty(mla.decode_workspace_bytes(B, s_q, H, scan_len), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    PART_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}[PART_DTYPE_NAME]
+
     def step(i, ev=None):
         c = caches[i % N_COPIES]
         if ev is not None:
@@ -436,12 +439,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if sparse:
-            mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws)
+            mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws, part_dtype=PART_DTYPE)
         else:
-            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws, fp8_math=f8m)
+            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws, fp8_math=f8m, part_dtype=PART_DTYPE)
         if ev is not None:
             ev[2].record(stream)
-        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1))
+        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1), part_dtype=PART_DTYPE)
         if ev is not None:
             ev[3].record(stream)
 
@@ -539,7 +542,8 @@ def main():
         "config": {"workload": f"{w.name}{' (E4M3 arithmetic)' if f8m else ''}: B={B} H={H} s_q={s_q} T={w.T or w.T_range}"
                                f"{f' top-{w.topk} selected' if sparse else ''} "
                                f"{'paged' if w.paged else 'contiguous'} {w.cache_dtype} latent cache [*, 576], "
-                               f"{'causal' if w.causal else 'non-causal'}, seed {w.seed}",
+                               f"{'causal' if w.causal else 'non-causal'}, {PART_DTYPE_NAME} split partials, "
+                               f"seed {w.seed}",
                    "global_batch": B, "seq_len": w.max_T, "parallelism": "single GPU"},
         "step_gbs": round(cnt["bytes_step"] / s / 1e9, 1),
         "tokens_per_s": round(N / s, 1),

@@ -18,10 +18,16 @@ namespace mla {
 namespace {
 
 // ---------------------------------------------------------------------------
-// absorb_q: grid (H, 4 column blocks of 128), 4 waves, wave w -> 32 columns.
+// absorb_q: grid (H x row groups of 64 query tokens, 4 column blocks of 128),
+// 4 waves, wave w -> 32 columns of both 32-row blocks.  Every global load of
+// a work-group (its weight slice, its query rows and, in column block 0, the
+// rope parts it carries over) is issued before the first wait, so a
+// work-group costs one memory round trip; the 64 rows of a group are spread
+// over the grid instead of looped over.
 // ---------------------------------------------------------------------------
 constexpr int AQ_COLS = 128;
 constexpr int AQ_CHUNKS = AQ_COLS * 2 / 16;   // 16 chunks per LDS row
+constexpr int AQ_ROWS = 64;                   // query tokens per work-group
 
 __device__ __forceinline__ int aq_off(int k, int c) {
   return (k * AQ_CHUNKS + ((c >> 3) ^ chunk_swz(k))) * 16 + (c & 7) * 2;
@@ -30,29 +36,14 @@ __device__ __forceinline__ int aq_off(int k, int c) {
 __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restrict__ q,
                                                        const uint16_t* __restrict__ w_uk,
                                                        uint16_t* __restrict__ q_lat, int N, int H) {
-  __shared__ __attribute__((aligned(1024))) char wt[D_NOPE * AQ_COLS * 2];   // 32 KB
-  __shared__ __attribute__((aligned(16))) uint16_t ot[32][AQ_COLS + 8];        // output block, padded
-  const int h = blockIdx.x, cblk = blockIdx.y;
+  __shared__ __attribute__((aligned(1024))) char wt[D_NOPE * AQ_COLS * 2];      // 32 KB
+  __shared__ __attribute__((aligned(16))) uint16_t ot[AQ_ROWS][AQ_COLS + 8];     // output block, padded
+  const int h = blockIdx.x % H, n0 = (blockIdx.x / H) * AQ_ROWS, cblk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int nblocks = (N + 31) / 32;
 
-  // query fragments of a 32-row block (8 k-steps of 16), loaded ahead of use
-  auto load_a = [&](int nb, i16x8 (&a)[D_NOPE / 16]) {
-    const int n = nb * 32 + l32;
-    const bool ok = n < N;
-    const uint16_t* qrow = q + ((int64_t)(ok ? n : 0) * H + h) * D_QK + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < D_NOPE / 16; ++ks) {
-      a[ks] = *(const i16x8*)(qrow + ks * 16);
-      if (!ok) a[ks] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  };
-  i16x8 abuf0[D_NOPE / 16], abuf1[D_NOPE / 16];
-  load_a(0, abuf0);
-
-  // stage W_UK[h][0:128][cblk*128 : +128]
+  // stage W_UK[h][0:128][cblk*128 : +128] (direct to LDS)
   {
     const uint16_t* src0 = w_uk + (int64_t)h * D_NOPE * D_C + cblk * AQ_COLS;
     char* dst = wt + wave * 64 * 16;
@@ -65,12 +56,29 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
                                        (lds_void_t*)(dst + i * 256 * 16), 16, 0, 0);
     }
   }
-  // rope part of the query rows is carried over unchanged
-  if (cblk == 0) {
-    for (int i = tid; i < N * (D_ROPE / 8); i += 256) {
-      const int n = i / (D_ROPE / 8), c8 = i % (D_ROPE / 8);
-      const int64_t qr = (int64_t)n * H + h;
-      *(i16x8*)(q_lat + qr * ROWW + D_C + c8 * 8) = *(const i16x8*)(q + qr * D_QK + D_NOPE + c8 * 8);
+  // query fragments of both 32-row blocks (8 k-steps of 16 each); rows past
+  // N re-read row n0 (always valid) and are zeroed after the wait
+  i16x8 a0[D_NOPE / 16], a1[D_NOPE / 16];
+  const bool ok0 = n0 + l32 < N, ok1 = n0 + 32 + l32 < N;
+  {
+    const uint16_t* r0 = q + ((int64_t)(ok0 ? n0 + l32 : n0) * H + h) * D_QK + half * 8;
+    const uint16_t* r1 = q + ((int64_t)(ok1 ? n0 + 32 + l32 : n0) * H + h) * D_QK + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D_NOPE / 16; ++ks) {
+      a0[ks] = *(const i16x8*)(r0 + ks * 16);
+      a1[ks] = *(const i16x8*)(r1 + ks * 16);
+    }
+  }
+  // rope parts of the group's rows (column block 0 only): 64 rows x 8 chunks
+  // of 16 B, two per thread, stored after the projection
+  i16x8 rope[2];
+  const int rr0 = tid >> 3, rc = tid & 7;             // rows rr0 and rr0 + 32, chunk rc
+  const bool rope_on = cblk == 0;
+  if (rope_on) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = n0 + rr0 + 32 * i;
+      rope[i] = *(const i16x8*)(q + ((int64_t)(n < N ? n : n0) * H + h) * D_QK + D_NOPE + rc * 8);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -79,38 +87,38 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   const int c0 = wave * 32;
   const int grp = (lane >> 4) & 1, jj = lane & 15;
   const int bcol = c0 + grp * 16 + 4 * (jj & 3);
-  bf16x8 bw[D_NOPE / 16];
+  f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < D_NOPE / 16; ++ks) {
     const int krow = ks * 16 + 8 * half + (jj >> 2);
-    bw[ks] = join_tr(ds_read_tr16(wt + aq_off(krow, bcol)), ds_read_tr16(wt + aq_off(krow + 4, bcol)));
+    const bf16x8 bw = join_tr(ds_read_tr16(wt + aq_off(krow, bcol)), ds_read_tr16(wt + aq_off(krow + 4, bcol)));
+    const i16x8 z = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    acc0 = mfma32(__builtin_bit_cast(bf16x8, ok0 ? a0[ks] : z), bw, acc0);
+    acc1 = mfma32(__builtin_bit_cast(bf16x8, ok1 ? a1[ks] : z), bw, acc1);
   }
-  auto block = [&](int nb, const i16x8 (&a)[D_NOPE / 16]) {
-    f32x16 acc = f32x16{};
+  // stage the 64 x 128 output block in LDS, then write whole 256-byte rows
 #pragma unroll
-    for (int ks = 0; ks < D_NOPE / 16; ++ks) acc = mfma32(__builtin_bit_cast(bf16x8, a[ks]), bw[ks], acc);
-    // stage the 32 x 128 output block in LDS, then write whole 256-byte rows
-    __syncthreads();   // previous block's rows have been written out
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * half + (r & 3);
+    ot[row][c0 + l32] = bf16_bits(to_bf16(acc0[r]));
+    ot[row + 32][c0 + l32] = bf16_bits(to_bf16(acc1[r]));
+  }
+  __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ot[8 * (r >> 2) + 4 * half + (r & 3)][c0 + l32] = bf16_bits(to_bf16(acc[r]));
-    __syncthreads();
+  for (int i = 0; i < 4; ++i) {
+    const int chunk = i * 256 + tid;          // 64 rows x 16 chunks of 16 B
+    const int rr = chunk >> 4, cc = chunk & 15;
+    const int nn = n0 + rr;
+    if (nn < N)
+      *(i16x8*)(q_lat + ((int64_t)nn * H + h) * ROWW + cblk * AQ_COLS + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+  }
+  // the rope part of the query rows is carried over unchanged
+  if (rope_on) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int chunk = i * 256 + tid;          // 32 rows x 16 chunks of 16 B
-      const int rr = chunk >> 4, cc = chunk & 15;
-      const int nn = nb * 32 + rr;
-      if (nn < N)
-        *(i16x8*)(q_lat + ((int64_t)nn * H + h) * ROWW + cblk * AQ_COLS + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+      const int n = n0 + rr0 + 32 * i;
+      if (n < N) *(i16x8*)(q_lat + ((int64_t)n * H + h) * ROWW + D_C + rc * 8) = rope[i];
     }
-  };
-  // two named fragment buffers, alternating (indexing an array of them by the
-  // block parity would place it in scratch memory)
-  for (int nb = 0; nb < nblocks; nb += 2) {
-    if (nb + 1 < nblocks) load_a(nb + 1, abuf1);
-    block(nb, abuf0);
-    if (nb + 1 >= nblocks) break;
-    if (nb + 2 < nblocks) load_a(nb + 2, abuf0);
-    block(nb + 1, abuf1);
   }
 }
 
@@ -247,7 +255,8 @@ __device__ __forceinline__ int co_aoff(int r, int k) {
   return r * (D_C * 2) + (((k >> 3) ^ (r & 15)) << 4) + (k & 7) * 2;
 }
 
-__global__ __launch_bounds__(256) void combine_out_kernel(const float* __restrict__ part_o,
+template <bool PB16>
+__global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict__ part_o,
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ seg_first,
                                                           const int32_t* __restrict__ seg_count,
@@ -292,38 +301,44 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
     const int n_split = seg_count[b];
     // splits are taken four at a time with every load of the group in flight
     // together (indices past the last split reload it and get weight 0), and
-    // added in split order
+    // added in split order.  The first group's partials are loaded with the
+    // log-sum-exps, before the maximum is known (it only sets their weights).
     constexpr int SG = 4;
+    auto load_group = [&](int s0, float (&l)[SG], PartRaw<PB16> (&d)[SG][NCH]) {
+#pragma unroll
+      for (int u = 0; u < SG; ++u) {
+        const int s = max(min(s0 + u, n_split - 1), 0);
+        l[u] = part_lse[(sb + s) * R + row];
+        const int64_t src = ((sb + s) * R + row) * D_C + cq;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) d[u][i] = part_load<PB16>(part_o, src + 4 * TPR * i);
+      }
+    };
+    float l[SG];
+    PartRaw<PB16> d[SG][NCH];
+    load_group(0, l, d);
     float mx = -INFINITY;
-    for (int s0 = 0; s0 < n_split; s0 += SG) {
-      float l[SG];
 #pragma unroll
-      for (int u = 0; u < SG; ++u) l[u] = part_lse[(sb + min(s0 + u, n_split - 1)) * R + row];
+    for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+    for (int s0 = SG; s0 < n_split; s0 += SG) {
 #pragma unroll
-      for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+      for (int u = 0; u < SG; ++u) mx = fmaxf(mx, part_lse[(sb + min(s0 + u, n_split - 1)) * R + row]);
     }
     float wsum = 0.f;
     f32x4 acc[NCH];
 #pragma unroll
     for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n_split; s0 += SG) {
+      if (s0 > 0) load_group(s0, l, d);
       float w[SG];
-      f32x4 d[SG][NCH];
 #pragma unroll
-      for (int u = 0; u < SG; ++u) {
-        const int s = min(s0 + u, n_split - 1);
-        const float ls = part_lse[(sb + s) * R + row];
-        w[u] = (s0 + u < n_split && ls != -INFINITY) ? exp2f(ls - mx) : 0.f;
-        const float* src = part_o + ((sb + s) * R + row) * D_C + cq;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) d[u][i] = *(const f32x4*)(src + 4 * TPR * i);
-      }
+      for (int u = 0; u < SG; ++u) w[u] = (s0 + u < n_split && l[u] != -INFINITY) ? exp2f(l[u] - mx) : 0.f;
 #pragma unroll
       for (int u = 0; u < SG; ++u) {
         if (w[u] == 0.f) continue;      // absent or empty split: its partial may hold anything
         wsum += w[u];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) acc[i] += w[u] * d[u][i];
+        for (int i = 0; i < NCH; ++i) acc[i] += w[u] * part_vals<PB16>(d[u][i]);
       }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
@@ -335,14 +350,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
       const int k = cq + 4 * TPR * i;
       if (ok && o_lat != nullptr) {
         const int64_t o = ((int64_t)n * H + h) * D_C + k;
-        if (o_bf16) {
-          const uint64_t packed = (uint64_t)bf16_bits(to_bf16(v[0])) | ((uint64_t)bf16_bits(to_bf16(v[1])) << 16) |
-                                  ((uint64_t)bf16_bits(to_bf16(v[2])) << 32) |
-                                  ((uint64_t)bf16_bits(to_bf16(v[3])) << 48);
-          *(uint64_t*)((uint16_t*)o_lat + o) = packed;
-        } else {
-          *(f32x4*)((float*)o_lat + o) = v;
-        }
+        part_store(o_lat, o, v, o_bf16 != 0);
       }
       // the projection sees the latent output at the precision the caller
       // asked for: bf16 as is, fp32 as high + low bf16 terms
@@ -413,18 +421,24 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_combine_out(const float* part_o, const float* part_lse, const int32_t* seg_first,
+hipError_t launch_combine_out(const void* part_o, int part_bf16, const float* part_lse, const int32_t* seg_first,
                               const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
   const int N = B * s_q;
-  hipLaunchKernelGGL(combine_out_kernel, dim3(H, (N + CO_ROWS - 1) / CO_ROWS), dim3(256), 0, stream, part_o,
-                     part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
+  const dim3 grid(H, (N + CO_ROWS - 1) / CO_ROWS);
+  if (part_bf16)
+    hipLaunchKernelGGL(combine_out_kernel<true>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count,
+                       s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
+  else
+    hipLaunchKernelGGL(combine_out_kernel<false>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first,
+                       seg_count, s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
   return hipGetLastError();
 }
 
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_lat, int N, int H,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(absorb_q_kernel, dim3(H, D_C / AQ_COLS), dim3(256), 0, stream, q, w_uk, q_lat, N, H);
+  const int groups = (N + AQ_ROWS - 1) / AQ_ROWS;
+  hipLaunchKernelGGL(absorb_q_kernel, dim3(H * groups, D_C / AQ_COLS), dim3(256), 0, stream, q, w_uk, q_lat, N, H);
   return hipGetLastError();
 }
 

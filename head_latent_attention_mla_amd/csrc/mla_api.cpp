@@ -204,12 +204,14 @@ namespace {
 // (contiguous bf16 caches only); sel_count / k_max replace the lengths
 mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                                int32_t H, float softmax_scale, int32_t causal, void* workspace,
-                               size_t ws_bytes, int32_t num_splits, hipStream_t st, bool fp8_math = false,
+                               size_t ws_bytes, int32_t num_splits, int32_t part_dtype, hipStream_t st,
+                               bool fp8_math = false,
                                const int32_t* sel_idx = nullptr, const int32_t* sel_count = nullptr,
                                int32_t k_max = 0) {
   if (q_lat == nullptr) return MLA_ERR_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || num_splits < 0) return MLA_ERR_ARG;
   if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (part_dtype != MLA_FP32 && part_dtype != MLA_BF16) return MLA_ERR_ARG;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
   const mla_status ks = check_kv(kv, s_q);
   if (ks != MLA_OK) return ks;
@@ -224,7 +226,8 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   p.row_scale = kv->row_scale;
   p.block_table = kv->block_table;
   p.seqlens = kv->seqlens;
-  p.part_o = (float*)workspace;
+  p.part_o = workspace;
+  p.part_bf16 = part_dtype == MLA_BF16;
   p.part_lse = (float*)((char*)workspace + pl.part_o_bytes);
   p.seg_first = (int32_t*)((char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
   p.seg_count = p.seg_first + B;
@@ -256,50 +259,51 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
 }
 
 mla_status decode_combine_impl(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                               int32_t num_splits, const void* workspace, size_t ws_bytes,
+                               int32_t num_splits, int32_t part_dtype, const void* workspace, size_t ws_bytes,
                                void* o_lat, int32_t o_lat_dtype, float* lse, hipStream_t st) {
   if (o_lat == nullptr) return MLA_ERR_ARG;
   if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  if (part_dtype != MLA_FP32 && part_dtype != MLA_BF16) return MLA_ERR_ARG;
   Plan pl;
   if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
-  const float* part_o = (const float*)workspace;
   const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
   const int32_t* seg_first = (const int32_t*)((const char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
-  return hip_status(mla::launch_combine(part_o, part_lse, seg_first, seg_first + B, B, pl.R, o_lat,
-                                        o_lat_dtype == MLA_BF16, lse, st));
+  return hip_status(mla::launch_combine(workspace, part_dtype == MLA_BF16, part_lse, seg_first, seg_first + B, B,
+                                        pl.R, o_lat, o_lat_dtype == MLA_BF16, lse, st));
 }
 
 }  // namespace
 
 mla_status mla_decode_partial(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                               int32_t H, float softmax_scale, int32_t causal, void* workspace,
-                              size_t ws_bytes, int32_t num_splits, void* stream) {
+                              size_t ws_bytes, int32_t num_splits, int32_t part_dtype, void* stream) {
   return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace, ws_bytes,
-                             num_splits, (hipStream_t)stream);
+                             num_splits, part_dtype, (hipStream_t)stream);
 }
 
 mla_status mla_decode_combine(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                              int32_t num_splits, const void* workspace, size_t ws_bytes,
+                              int32_t num_splits, int32_t part_dtype, const void* workspace, size_t ws_bytes,
                               void* o_lat, int32_t o_lat_dtype, float* lse, void* stream) {
-  return decode_combine_impl(B, s_q, H, max_seqlen, num_splits, workspace, ws_bytes, o_lat,
+  return decode_combine_impl(B, s_q, H, max_seqlen, num_splits, part_dtype, workspace, ws_bytes, o_lat,
                              o_lat_dtype, lse, (hipStream_t)stream);
 }
 
 mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                                  int32_t num_splits, const void* workspace, size_t ws_bytes,
+                                  int32_t num_splits, int32_t part_dtype, const void* workspace, size_t ws_bytes,
                                   const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
                                   float* lse, void* stream) {
   if (w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;
   if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  if (part_dtype != MLA_FP32 && part_dtype != MLA_BF16) return MLA_ERR_ARG;
   Plan pl;
   if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return MLA_ERR_ARG;
   if ((int64_t)B * s_q * H > (1 << 26)) return MLA_ERR_ARG;
   if (workspace == nullptr || ws_bytes < pl.ws_bytes) return MLA_ERR_WORKSPACE;
-  const float* part_o = (const float*)workspace;
   const float* part_lse = (const float*)((const char*)workspace + pl.part_o_bytes);
   const int32_t* seg_first = (const int32_t*)((const char*)workspace + pl.part_o_bytes + pl.part_lse_bytes);
-  return hip_status(mla::launch_combine_out(part_o, part_lse, seg_first, seg_first + B, B, s_q, H,
+  return hip_status(mla::launch_combine_out(workspace, part_dtype == MLA_BF16, part_lse, seg_first, seg_first + B,
+                                            B, s_q, H,
                                             (const uint16_t*)w_uv, (uint16_t*)out, o_lat,
                                             o_lat_dtype == MLA_BF16, lse, (hipStream_t)stream));
 }
@@ -311,10 +315,11 @@ mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, 
   // validate the outputs too before anything is enqueued
   if (o_lat == nullptr) return MLA_ERR_ARG;
   if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  // the partials are kept in the precision asked for the latent output
   const mla_status s = decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace,
-                                           ws_bytes, num_splits, (hipStream_t)stream);
+                                           ws_bytes, num_splits, o_lat_dtype, (hipStream_t)stream);
   if (s != MLA_OK) return s;
-  return decode_combine_impl(B, s_q, H, kv->max_seqlen, num_splits, workspace, ws_bytes, o_lat,
+  return decode_combine_impl(B, s_q, H, kv->max_seqlen, num_splits, o_lat_dtype, workspace, ws_bytes, o_lat,
                              o_lat_dtype, lse, (hipStream_t)stream);
 }
 
@@ -357,8 +362,9 @@ size_t mla_sparse_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t k_m
 mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv, const int32_t* sel_idx,
                                      const int32_t* sel_count, int32_t k_max, int32_t B, int32_t s_q,
                                      int32_t H, float softmax_scale, void* workspace, size_t ws_bytes,
-                                     int32_t num_splits, void* stream) {
+                                     int32_t num_splits, int32_t part_dtype, void* stream) {
   if (q_lat == nullptr || sel_idx == nullptr || sel_count == nullptr) return MLA_ERR_ARG;
+  if (part_dtype != MLA_FP32 && part_dtype != MLA_BF16) return MLA_ERR_ARG;
   if (B <= 0 || s_q <= 0 || H <= 0 || k_max <= 0 || num_splits < 0) return MLA_ERR_ARG;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
   const mla_status ks = check_kv(kv, 1);
@@ -373,7 +379,7 @@ mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv, c
   // the scan gathers the selected rows itself
   if (kv->block_table == nullptr && !fp8 && (int64_t)kv->T_stride * mla::ROWW * 2 <= ((int64_t)1 << 30))
     return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, 0, workspace, pl.ws_bytes, num_splits,
-                               (hipStream_t)stream, false, sel_idx, sel_count, k_max);
+                               part_dtype, (hipStream_t)stream, false, sel_idx, sel_count, k_max);
   mla::GatherParams g{};
   g.rows = kv->rows;
   g.row_scale = kv->row_scale;
@@ -403,7 +409,7 @@ mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv, c
   compact.max_blocks = 0;
   compact.max_seqlen = k_max;
   return decode_partial_impl(q_lat, &compact, B, s_q, H, softmax_scale, 0, workspace, pl.ws_bytes, num_splits,
-                             (hipStream_t)stream);
+                             part_dtype, (hipStream_t)stream);
 }
 
 mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv, const int32_t* sel_idx,
@@ -413,10 +419,10 @@ mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv, cons
   if (o_lat == nullptr) return MLA_ERR_ARG;
   if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
   const mla_status s = mla_sparse_decode_partial(q_lat, kv, sel_idx, sel_count, k_max, B, s_q, H, softmax_scale,
-                                                 workspace, ws_bytes, num_splits, stream);
+                                                 workspace, ws_bytes, num_splits, o_lat_dtype, stream);
   if (s != MLA_OK) return s;
-  return decode_combine_impl(B, s_q, H, k_max, num_splits, workspace, ws_bytes, o_lat, o_lat_dtype, lse,
-                             (hipStream_t)stream);
+  return decode_combine_impl(B, s_q, H, k_max, num_splits, o_lat_dtype, workspace, ws_bytes, o_lat, o_lat_dtype,
+                             lse, (hipStream_t)stream);
 }
 
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
@@ -553,17 +559,18 @@ mla_status mla_attend(const void* q, const mla_kv_desc* kv, const void* w_uk, co
   const size_t dws_bytes = ws_bytes - ql_bytes;
   mla_status s = mla_absorb_q(q, w_uk, q_lat, B * s_q, H, mla::D_NOPE, mla::D_ROPE, mla::D_C, stream);
   if (s != MLA_OK) return s;
-  s = decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, dws, dws_bytes, 0, st);
+  // bf16 partials: the output is bf16
+  s = decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, dws, dws_bytes, 0, MLA_BF16, st);
   if (s != MLA_OK) return s;
-  return mla_decode_combine_out(B, s_q, H, kv->max_seqlen, 0, dws, dws_bytes, w_uv, out, nullptr, MLA_FP32,
-                                nullptr, stream);
+  return mla_decode_combine_out(B, s_q, H, kv->max_seqlen, 0, MLA_BF16, dws, dws_bytes, w_uv, out, nullptr,
+                                MLA_FP32, nullptr, stream);
 }
 
 mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q, int32_t H,
                                   float softmax_scale, int32_t causal, void* workspace, size_t ws_bytes,
-                                  int32_t num_splits, void* stream) {
+                                  int32_t num_splits, int32_t part_dtype, void* stream) {
   return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace, ws_bytes, num_splits,
-                             (hipStream_t)stream, true);
+                             part_dtype, (hipStream_t)stream, true);
 }
 
 }  // extern "C"

@@ -110,6 +110,39 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 
+// Split partial outputs: four consecutive values of a partial row, stored as
+// fp32 or as bf16 (rounded to nearest even).  PartRaw is what a load returns
+// (the values still packed), part_vals unpacks it.
+template <bool PB16>
+using PartRaw = typename std::conditional<PB16, uint64_t, f32x4>::type;
+
+template <bool PB16>
+__device__ __forceinline__ PartRaw<PB16> part_load(const void* base, int64_t elem) {
+  if constexpr (PB16) return *(const uint64_t*)((const uint16_t*)base + elem);
+  else return *(const f32x4*)((const float*)base + elem);
+}
+
+template <bool PB16>
+__device__ __forceinline__ f32x4 part_vals(PartRaw<PB16> r) {
+  if constexpr (PB16) {
+    const uint32_t lo = (uint32_t)r, hi = (uint32_t)(r >> 32);
+    return f32x4{__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                 __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xFFFF0000u)};
+  } else {
+    return r;
+  }
+}
+
+__device__ __forceinline__ uint64_t pack_bf16x4(f32x4 v) {
+  return (uint64_t)bf16_bits(to_bf16(v[0])) | ((uint64_t)bf16_bits(to_bf16(v[1])) << 16) |
+         ((uint64_t)bf16_bits(to_bf16(v[2])) << 32) | ((uint64_t)bf16_bits(to_bf16(v[3])) << 48);
+}
+
+__device__ __forceinline__ void part_store(void* base, int64_t elem, f32x4 v, bool pb16) {
+  if (pb16) *(uint64_t*)((uint16_t*)base + elem) = pack_bf16x4(v);
+  else *(f32x4*)((float*)base + elem) = v;
+}
+
 // Work-group barriers that wait only for what the barrier publishes.
 // __syncthreads() would also wait for the prefetch of the next tile (vmcnt).
 __device__ __forceinline__ void barrier_tile_ready() {

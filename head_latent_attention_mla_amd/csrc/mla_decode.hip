@@ -589,7 +589,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 
   // partial rows are row-major [slot][R][512], slot = k + b (unique: along
   // the plan, k and b never both stay put); a lane pair covers 128
-  // contiguous bytes of one row per (cb, rb), stored back to back
+  // contiguous bytes of one row per (cb, rb) (64 as bf16), stored back to back
   const int64_t pbase = (int64_t)sl * p.R;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) {
@@ -597,14 +597,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     if (row >= p.R) continue;
     const float l = lsh[rb * 32 + l32];
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    float* prow = p.part_o + (pbase + row) * D_C + wave * 128 + 4 * half;
+    const int64_t prow = (pbase + row) * D_C + wave * 128 + 4 * half;   // element index
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v = {acc[cb][rb][4 * q4] * inv, acc[cb][rb][4 * q4 + 1] * inv,
                          acc[cb][rb][4 * q4 + 2] * inv, acc[cb][rb][4 * q4 + 3] * inv};
-        *(f32x4*)(prow + cb * 32 + 8 * q4) = v;
+        part_store(p.part_o, prow + cb * 32 + 8 * q4, v, p.part_bf16 != 0);
       }
     }
   }
@@ -616,7 +616,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 // 2^(lse_s - max_s), then the weighted mean of the normalised partial rows.
 // One thread per (row, 4 latent columns); partial and output rows are
 // contiguous, so every load and store is coalesced.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+template <bool PB16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ part_o,
                                                       const float* __restrict__ part_lse,
                                                       const int32_t* __restrict__ seg_first,
                                                       const int32_t* __restrict__ seg_count, int B, int R,
@@ -628,47 +629,45 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c4 = (threadIdx.x & 127) * 4;
   const int64_t s0 = seg_first[b];
   const int ns = seg_count[b];
-  // splits four at a time, all loads of a group in flight together; added in
-  // split order (the same order and arithmetic as combine_out_kernel's merge)
+  // splits four at a time, all loads of a group in flight together (the
+  // first group's with the log-sum-exps); added in split order (the same
+  // order and arithmetic as combine_out_kernel's merge)
   constexpr int SG = 4;
+  float l[SG];
+  PartRaw<PB16> d[SG];
+  auto load_group = [&](int g0) {
+#pragma unroll
+    for (int u = 0; u < SG; ++u) {
+      const int s = max(min(g0 + u, ns - 1), 0);
+      l[u] = part_lse[(s0 + s) * R + row];
+      d[u] = part_load<PB16>(part_o, ((s0 + s) * R + row) * D_C + c4);
+    }
+  };
+  load_group(0);
   float mx = -INFINITY;
-  for (int g0 = 0; g0 < ns; g0 += SG) {
-    float l[SG];
 #pragma unroll
-    for (int u = 0; u < SG; ++u) l[u] = part_lse[(s0 + min(g0 + u, ns - 1)) * R + row];
+  for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+  for (int g0 = SG; g0 < ns; g0 += SG) {
 #pragma unroll
-    for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
+    for (int u = 0; u < SG; ++u) mx = fmaxf(mx, part_lse[(s0 + min(g0 + u, ns - 1)) * R + row]);
   }
   float wsum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int g0 = 0; g0 < ns; g0 += SG) {
+    if (g0 > 0) load_group(g0);
     float w[SG];
-    f32x4 d[SG];
 #pragma unroll
-    for (int u = 0; u < SG; ++u) {
-      const int s = min(g0 + u, ns - 1);
-      const float ls = part_lse[(s0 + s) * R + row];
-      w[u] = (g0 + u < ns && ls != -INFINITY) ? exp2f(ls - mx) : 0.f;
-      d[u] = *(const f32x4*)(part_o + ((s0 + s) * R + row) * D_C + c4);
-    }
+    for (int u = 0; u < SG; ++u) w[u] = (g0 + u < ns && l[u] != -INFINITY) ? exp2f(l[u] - mx) : 0.f;
 #pragma unroll
     for (int u = 0; u < SG; ++u) {
       if (w[u] == 0.f) continue;
       wsum += w[u];
-      acc += w[u] * d[u];
+      acc += w[u] * part_vals<PB16>(d[u]);
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   acc *= inv;
-  if (o_bf16) {
-    const uint64_t packed = (uint64_t)bf16_bits(to_bf16(acc[0])) |
-                            ((uint64_t)bf16_bits(to_bf16(acc[1])) << 16) |
-                            ((uint64_t)bf16_bits(to_bf16(acc[2])) << 32) |
-                            ((uint64_t)bf16_bits(to_bf16(acc[3])) << 48);
-    *(uint64_t*)((uint16_t*)o_lat + row_g * D_C + c4) = packed;
-  } else {
-    *(f32x4*)((float*)o_lat + row_g * D_C + c4) = acc;
-  }
+  part_store(o_lat, row_g * D_C + c4, acc, o_bf16 != 0);
   if (lse_out != nullptr && (threadIdx.x & 127) == 0)
     lse_out[row_g] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
 }
@@ -695,12 +694,17 @@ hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
+hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_lse, const int32_t* seg_first,
                           const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,
                           hipStream_t stream) {
   const int64_t rows = (int64_t)B * R;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, part_o, part_lse,
-                     seg_first, seg_count, B, R, o_lat, o_bf16, lse);
+  const dim3 grid((unsigned)((rows + 1) / 2));
+  if (part_bf16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count, B,
+                       R, o_lat, o_bf16, lse);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count, B,
+                       R, o_lat, o_bf16, lse);
   return hipGetLastError();
 }
 

@@ -445,14 +445,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     if (row >= p.R) continue;
     const float l = lsh[rb * 32 + l32];
     const float inv = l > 0.f ? unscale / l : 0.f;
-    float* prow = p.part_o + (pbase + row) * D_C + wave * 128 + 4 * half;
+    const int64_t prow = (pbase + row) * D_C + wave * 128 + 4 * half;   // element index
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const f32x4 v = {acc[cb][rb][4 * q4] * inv, acc[cb][rb][4 * q4 + 1] * inv,
                          acc[cb][rb][4 * q4 + 2] * inv, acc[cb][rb][4 * q4 + 3] * inv};
-        *(f32x4*)(prow + cb * 32 + 8 * q4) = v;
+        part_store(p.part_o, prow + cb * 32 + 8 * q4, v, p.part_bf16 != 0);
       }
     }
   }

@@ -23,7 +23,7 @@ struct DecodeParams {
   const float* row_scale;       // e4m3 only
   const int32_t* block_table;   // paged only
   const int32_t* seqlens;       // [B]
-  float* part_o;                // fp32 [n_ranges + B, R, 512], normalised partial outputs
+  void* part_o;                 // [n_ranges + B, R, 512] normalised partial outputs, fp32 or bf16
   float* part_lse;              // fp32 [n_ranges + B, R], log2-domain log-sum-exp
   int32_t* seg_first;           // [B] first partial slot of each sequence
   int32_t* seg_count;           // [B] number of partial slots of each sequence
@@ -42,6 +42,7 @@ struct DecodeParams {
   const int32_t* sel_idx;       // [B, k_max] selected positions, or null
   const int32_t* src_len;       // [B] cache lengths
   int32_t k_max;
+  int32_t part_bf16;            // partial outputs stored as bf16 (else fp32)
 };
 
 // One call of the naive (expand-then-attend) ablation.
@@ -127,14 +128,15 @@ struct PrefillParams {
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
-hipError_t launch_combine(const float* part_o, const float* part_lse, const int32_t* seg_first,
+// part_o: fp32 partials, or bf16 when part_bf16 is set
+hipError_t launch_combine(const void* part_o, int part_bf16, const float* part_lse, const int32_t* seg_first,
                           const int32_t* seg_count, int B, int R, void* o_lat, int o_bf16, float* lse,
                           hipStream_t stream);
 hipError_t launch_absorb_q(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_lat, int N, int H,
                            hipStream_t stream);
 hipError_t launch_absorb_out(const void* o_lat, int o_bf16, const uint16_t* w_uv, uint16_t* out,
                              int N, int H, hipStream_t stream);
-hipError_t launch_combine_out(const float* part_o, const float* part_lse, const int32_t* seg_first,
+hipError_t launch_combine_out(const void* part_o, int part_bf16, const float* part_lse, const int32_t* seg_first,
                               const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream);
 hipError_t launch_naive(const NaiveParams& p, hipStream_t stream);

@@ -57,15 +57,16 @@ SIGNATURES = {
     "mla_decode_attn": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _I32,
                                _VP, _VP, _SZ, _I32, _VP]),
     "mla_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ, _I32,
-                                  _VP]),
+                                  _I32, _VP]),
     "mla_decode_partial_fp8": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ,
-                                      _I32, _VP]),
-    "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
+                                      _I32, _I32, _VP]),
+    "mla_decode_combine": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _I32, _VP, _VP]),
     "mla_absorb_out": (_I32, [_VP, _I32, _VP, _VP, _I32, _I32, _I32, _I32, _VP]),
-    "mla_decode_combine_out": (_I32, [_I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, _I32, _VP, _VP]),
+    "mla_decode_combine_out": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32, _VP, _SZ, _VP, _VP, _VP, _I32, _VP,
+                                      _VP]),
     "mla_sparse_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "mla_sparse_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _I32, _F32,
-                                         _VP, _SZ, _I32, _VP]),
+                                         _VP, _SZ, _I32, _I32, _VP]),
     "mla_sparse_decode_attn": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _I32, _F32,
                                       _VP, _I32, _VP, _VP, _SZ, _I32, _VP]),
     "mla_naive_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
@@ -232,11 +233,17 @@ def decode_attn(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_
     return o_lat, lse
 
 
+def _part_code(part_dtype) -> int:
+    """Element type of the split partials: torch.float32 or torch.bfloat16."""
+    return {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[part_dtype]
+
+
 def decode_partial(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_SCALE, causal: bool = False,
                    num_splits: int = 0, workspace: Optional[torch.Tensor] = None, stream=None,
-                   fp8_math: bool = False) -> torch.Tensor:
+                   fp8_math: bool = False, part_dtype=torch.float32) -> torch.Tensor:
     """Phase 1 of decode_attn: the split-T scan into a workspace (returned).
-    fp8_math (FP8 caches only): E4M3 matrix arithmetic (mla_decode_partial_fp8)."""
+    fp8_math (FP8 caches only): E4M3 matrix arithmetic (mla_decode_partial_fp8).
+    part_dtype: element type of the partials (pass the same to the merge)."""
     B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
     _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
     kv = cache.desc()
@@ -246,13 +253,13 @@ def decode_partial(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAU
     fn, name = ((_lib.mla_decode_partial_fp8, "mla_decode_partial_fp8") if fp8_math
                 else (_lib.mla_decode_partial, "mla_decode_partial"))
     _check(fn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
-              _ptr(workspace), workspace.numel(), num_splits, _stream(stream)), name)
+              _ptr(workspace), workspace.numel(), num_splits, _part_code(part_dtype), _stream(stream)), name)
     return workspace
 
 
 def decode_combine(workspace: torch.Tensor, B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0,
                    o_dtype=torch.float32, o_lat: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, stream=None):
+                   lse: Optional[torch.Tensor] = None, stream=None, part_dtype=torch.float32):
     """Phase 2 of decode_attn: merge the split partials held in ``workspace``."""
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
     if o_lat is None:
@@ -260,14 +267,16 @@ def decode_combine(workspace: torch.Tensor, B: int, s_q: int, H: int, max_seqlen
     _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
     if lse is not None:
         _require(lse, "lse", torch.float32, (B, s_q, H))
-    _check(_lib.mla_decode_combine(B, s_q, H, max_seqlen, num_splits, _ptr(workspace), workspace.numel(),
+    _check(_lib.mla_decode_combine(B, s_q, H, max_seqlen, num_splits, _part_code(part_dtype), _ptr(workspace),
+                                   workspace.numel(),
                                    _ptr(o_lat), dt, _ptr(lse), _stream(stream)), "mla_decode_combine")
     return o_lat, lse
 
 
 def decode_combine_out(workspace: torch.Tensor, w_uv: torch.Tensor, B: int, s_q: int, H: int, max_seqlen: int,
                        num_splits: int = 0, o_dtype=torch.float32, out: Optional[torch.Tensor] = None,
-                       o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None):
+                       o_lat: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None, stream=None,
+                       part_dtype=torch.float32):
     """Phases 2 + 4 fused: merge the split partials and project through W_UV.
     Returns out [B * s_q, H, 128] bf16; o_lat and lse are written when given."""
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
@@ -279,7 +288,8 @@ def decode_combine_out(workspace: torch.Tensor, w_uv: torch.Tensor, B: int, s_q:
         _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
     if lse is not None:
         _require(lse, "lse", torch.float32, (B, s_q, H))
-    _check(_lib.mla_decode_combine_out(B, s_q, H, max_seqlen, num_splits, _ptr(workspace), workspace.numel(),
+    _check(_lib.mla_decode_combine_out(B, s_q, H, max_seqlen, num_splits, _part_code(part_dtype), _ptr(workspace),
+                                       workspace.numel(),
                                        _ptr(w_uv), _ptr(out), _ptr(o_lat), dt, _ptr(lse), _stream(stream)),
            "mla_decode_combine_out")
     return out
@@ -301,15 +311,19 @@ def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
 
 def decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.Tensor,
            scale: float = DEFAULT_SCALE, causal: bool = False, o_dtype=torch.float32,
-           num_splits: int = 0, fused: bool = True, stream=None, fp8_math: bool = False) -> torch.Tensor:
+           num_splits: int = 0, fused: bool = True, stream=None, fp8_math: bool = False,
+           part_dtype=torch.bfloat16) -> torch.Tensor:
     """Absorbed MLA decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16.
-    fused: merge and project in one pass (mla_decode_combine_out); otherwise
-    mla_decode_attn then mla_absorb_out.  Both give the same bits."""
+    fused: merge and project in one pass (mla_decode_combine_out) with split
+    partials of part_dtype; otherwise mla_decode_attn (partials in o_dtype)
+    then mla_absorb_out.  Both give the same bits when part_dtype == o_dtype."""
     B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
     q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
     if fused or fp8_math:
-        ws = decode_partial(q_lat, cache, scale, causal, num_splits, stream=stream, fp8_math=fp8_math)
-        out = decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, num_splits, o_dtype, stream=stream)
+        ws = decode_partial(q_lat, cache, scale, causal, num_splits, stream=stream, fp8_math=fp8_math,
+                            part_dtype=part_dtype)
+        out = decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, num_splits, o_dtype, stream=stream,
+                                 part_dtype=part_dtype)
         return out.view(B, s_q, H, D_V)
     o_lat, _ = decode_attn(q_lat, cache, scale, causal, o_dtype, num_splits, want_lse=False, stream=stream)
     return absorb_out(o_lat.view(B * s_q, H, D_C), w_uv, stream=stream).view(B, s_q, H, D_V)
@@ -331,7 +345,8 @@ def _sparse_args(q_lat, cache, sel_idx, sel_count):
 
 def sparse_decode_partial(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torch.Tensor, sel_count: torch.Tensor,
                           scale: float = DEFAULT_SCALE, num_splits: int = 0,
-                          workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                          workspace: Optional[torch.Tensor] = None, stream=None,
+                          part_dtype=torch.float32) -> torch.Tensor:
     """Sparse top-k scan into a workspace (returned): attention over the rows
     sel_idx[b, :sel_count[b]] of each sequence.  Merge with decode_combine /
     decode_combine_out using k_max = sel_idx.shape[1] as max_seqlen."""
@@ -342,7 +357,7 @@ def sparse_decode_partial(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torc
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
     _check(_lib.mla_sparse_decode_partial(_ptr(q_lat), ctypes.byref(kv), _ptr(sel_idx), _ptr(sel_count), k_max,
                                           B, s_q, H, float(scale), _ptr(workspace), workspace.numel(), num_splits,
-                                          _stream(stream)), "mla_sparse_decode_partial")
+                                          _part_code(part_dtype), _stream(stream)), "mla_sparse_decode_partial")
     return workspace
 
 
@@ -366,12 +381,14 @@ def sparse_decode_attn(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torch.T
 
 def sparse_decode(q: torch.Tensor, cache: LatentCache, sel_idx: torch.Tensor, sel_count: torch.Tensor,
                   w_uk: torch.Tensor, w_uv: torch.Tensor, scale: float = DEFAULT_SCALE, num_splits: int = 0,
-                  stream=None) -> torch.Tensor:
+                  stream=None, part_dtype=torch.bfloat16) -> torch.Tensor:
     """Sparse absorbed decode: q [B, s_q, H, 192] -> out [B, s_q, H, 128] bf16."""
     B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
     q_lat = absorb_q(q.view(B * s_q, H, -1), w_uk, stream=stream).view(B, s_q, H, ROW)
-    ws = sparse_decode_partial(q_lat, cache, sel_idx, sel_count, scale, num_splits, stream=stream)
-    out = decode_combine_out(ws, w_uv, B, s_q, H, int(sel_idx.shape[1]), num_splits, stream=stream)
+    ws = sparse_decode_partial(q_lat, cache, sel_idx, sel_count, scale, num_splits, stream=stream,
+                               part_dtype=part_dtype)
+    out = decode_combine_out(ws, w_uv, B, s_q, H, int(sel_idx.shape[1]), num_splits, stream=stream,
+                             part_dtype=part_dtype)
     return out.view(B, s_q, H, D_V)
 
 

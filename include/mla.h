@@ -159,12 +159,16 @@ mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
  * were scanned on different devices).  mla_decode_attn is exactly
  * mla_decode_partial followed by mla_decode_combine on the same workspace.
  *
- * mla_decode_partial: same arguments as mla_decode_attn minus the outputs.
+ * mla_decode_partial: same arguments as mla_decode_attn minus the outputs,
+ *   plus part_dtype, the element type of the partial outputs: MLA_FP32, or
+ *   MLA_BF16 (each value rounded to nearest even: half the partial traffic,
+ *   about 2^-9 relative error on each partial; mla_decode_attn uses the
+ *   precision of its o_lat_dtype).  Any other value gives MLA_ERR_ARG.
  *   Scans every part and writes into the workspace, with
  *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits),
  *   R = s_q * H and M = B * (S + 1) partial slots (aligned = rounded up to a
  *   multiple of 256 bytes):
- *     part_o    fp32 [M, R, 512] at offset 0: slot m holds the normalised
+ *     part_o    part_dtype [M, R, 512] at offset 0: slot m holds the normalised
  *               partial latent output of one part for each of the R rows;
  *     part_lse  fp32 [M, R] at aligned(M * R * 512 * 4): the base-2
  *               log-sum-exp of the part's scaled scores (-inf when it holds
@@ -172,18 +176,21 @@ mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
  *     seg_first int32 [B], then seg_count int32 [B], at aligned(...) after
  *               part_lse: sequence b's parts are the slots seg_first[b] ..
  *               seg_first[b] + seg_count[b] - 1, in row order.
- *   Slots outside every sequence's run are left unwritten.
+ *   The offsets do not depend on part_dtype (bf16 partials use the first half
+ *   of the part_o region).  Slots outside every sequence's run are left
+ *   unwritten.
  * mla_decode_combine: merges the parts of every query row with weights
  *   2^(lse_s - max_s lse_s) and writes o_lat and (if not NULL) the natural-log
- *   lse, exactly as mla_decode_attn does.  B, s_q, H, max_seqlen and
- *   num_splits must be those given to mla_decode_partial. */
+ *   lse, exactly as mla_decode_attn does.  B, s_q, H, max_seqlen, num_splits
+ *   and part_dtype must be those given to mla_decode_partial. */
 mla_status mla_decode_partial(const void* q_lat, const mla_kv_desc* kv,
                               int32_t B, int32_t s_q, int32_t H,
                               float softmax_scale, int32_t causal,
                               void* workspace, size_t ws_bytes, int32_t num_splits,
-                              void* stream);
+                              int32_t part_dtype, void* stream);
 mla_status mla_decode_combine(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                              int32_t num_splits, const void* workspace, size_t ws_bytes,
+                              int32_t num_splits, int32_t part_dtype,
+                              const void* workspace, size_t ws_bytes,
                               void* o_lat, int32_t o_lat_dtype, float* lse, void* stream);
 
 /* Step 4 -- project the latent output back per head ("MLA, dim by dim",
@@ -205,8 +212,8 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
  * (the value order of "MLA, dim by dim", "MLA Decode": the latent output of
  * each head goes straight through W_UV[h]).  The result is bitwise equal to
  * mla_decode_combine followed by mla_absorb_out with the same o_lat_dtype.
- *   B, s_q, H, max_seqlen, num_splits, workspace, ws_bytes: as given to
- *          mla_decode_partial (the workspace holds its partials).
+ *   B, s_q, H, max_seqlen, num_splits, part_dtype, workspace, ws_bytes: as
+ *          given to mla_decode_partial (the workspace holds its partials).
  *   w_uv   bf16 [H, 512, 128]
  *   out    bf16 [B * s_q, H, 128]
  *   o_lat  NULL, or [B, s_q, H, 512] of o_lat_dtype: also written when given.
@@ -215,7 +222,8 @@ mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_
  *          o_lat is written.
  *   lse    NULL or fp32 [B, s_q, H], natural log. */
 mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                                  int32_t num_splits, const void* workspace, size_t ws_bytes,
+                                  int32_t num_splits, int32_t part_dtype,
+                                  const void* workspace, size_t ws_bytes,
                                   const void* w_uv, void* out, void* o_lat, int32_t o_lat_dtype,
                                   float* lse, void* stream);
 
@@ -233,7 +241,7 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
 mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int32_t B,
                                   int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
                                   void* workspace, size_t ws_bytes, int32_t num_splits,
-                                  void* stream);
+                                  int32_t part_dtype, void* stream);
 
 /* Sparse top-k decode ("Why MLA and MTP Fight Each Other", section 6: a
  * selector keeps the top-k cached latents and attention runs over those only,
@@ -257,15 +265,18 @@ mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int3
  *              num_splits, kv->dtype).  Its first part has the layout of
  *              mla_decode_partial's workspace with max_seqlen = k_max, so
  *              mla_decode_combine and mla_decode_combine_out (given k_max as
- *              max_seqlen) merge the partials of mla_sparse_decode_partial.
- * mla_sparse_decode_attn = mla_sparse_decode_partial + mla_decode_combine. */
+ *              max_seqlen and the same part_dtype) merge the partials of
+ *              mla_sparse_decode_partial.
+ *   part_dtype MLA_FP32 or MLA_BF16 partials, as for mla_decode_partial.
+ * mla_sparse_decode_attn = mla_sparse_decode_partial + mla_decode_combine,
+ * with partials in the precision of o_lat_dtype. */
 size_t mla_sparse_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t k_max,
                                   int32_t num_splits, int32_t cache_dtype);
 mla_status mla_sparse_decode_partial(const void* q_lat, const mla_kv_desc* kv,
                                      const int32_t* sel_idx, const int32_t* sel_count,
                                      int32_t k_max, int32_t B, int32_t s_q, int32_t H,
                                      float softmax_scale, void* workspace, size_t ws_bytes,
-                                     int32_t num_splits, void* stream);
+                                     int32_t num_splits, int32_t part_dtype, void* stream);
 mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv,
                                   const int32_t* sel_idx, const int32_t* sel_count,
                                   int32_t k_max, int32_t B, int32_t s_q, int32_t H,
@@ -363,7 +374,8 @@ mla_status mla_prefill_expand(const void* q, const mla_kv_desc* kv, const void* 
  * Fight Each Other", section 5.6): the expand path is used when
  *   s_q >= S*(L) = L d_c (d_k + d_v) / (d_c (d_k + d_v) + L (2 d_c - d_k - d_v)),
  * L = max_seqlen (S* is 128 at L = 512 and tends to 170.7), else the absorbed
- * path (mla_absorb_q, mla_decode_partial, mla_decode_combine_out).
+ * path (mla_absorb_q, mla_decode_partial with bf16 partials,
+ * mla_decode_combine_out).
  * mla_attend_uses_expand returns 1 (expand), 0 (absorbed) or -1 (bad sizes).
  * mla_attend takes the inputs and output of mla_prefill_expand and a
  * workspace of mla_attend_workspace_bytes(...) for the path it picks. */

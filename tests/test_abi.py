@@ -148,12 +148,13 @@ def test_naive_rejects_bad_arguments(m):
 def test_combine_out_rejects_bad_arguments(m):
     co = m._lib.mla_decode_combine_out
     need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
-    assert co(2, 1, 16, 256, 0, 0x1000, need, None, 0x2000, None, 2, None, None) == ARG     # no w_uv
-    assert co(2, 1, 16, 256, 0, 0x1000, need, 0x3000, None, None, 2, None, None) == ARG     # no out
-    assert co(2, 1, 16, 256, 0, 0x1000, need, 0x3000, 0x2000, None, 1, None, None) == ARG   # fp8 o_lat
-    assert co(0, 1, 16, 256, 0, 0x1000, need, 0x3000, 0x2000, None, 2, None, None) == ARG
-    assert co(2, 1, 16, 256, 0, 0x1000, need - 1, 0x3000, 0x2000, None, 2, None, None) == WS
-    assert co(2, 1, 16, 256, 0, None, need, 0x3000, 0x2000, None, 2, None, None) == WS
+    assert co(2, 1, 16, 256, 0, 2, 0x1000, need, None, 0x2000, None, 2, None, None) == ARG     # no w_uv
+    assert co(2, 1, 16, 256, 0, 2, 0x1000, need, 0x3000, None, None, 2, None, None) == ARG     # no out
+    assert co(2, 1, 16, 256, 0, 2, 0x1000, need, 0x3000, 0x2000, None, 1, None, None) == ARG   # fp8 o_lat
+    assert co(0, 1, 16, 256, 0, 2, 0x1000, need, 0x3000, 0x2000, None, 2, None, None) == ARG
+    assert co(2, 1, 16, 256, 0, 2, 0x1000, need - 1, 0x3000, 0x2000, None, 2, None, None) == WS
+    assert co(2, 1, 16, 256, 0, 2, None, need, 0x3000, 0x2000, None, 2, None, None) == WS
+    assert co(2, 1, 16, 256, 0, 1, 0x1000, need, 0x3000, 0x2000, None, 2, None, None) == ARG   # fp8 partials
 
 
 def test_sparse_rejects_bad_arguments(m):
@@ -164,12 +165,13 @@ def test_sparse_rejects_bad_arguments(m):
     assert wsb(2, 1, 16, 0, 0, 0) == 0 and wsb(2, 1, 16, 64, 0, 2) == 0
     sp = m._lib.mla_sparse_decode_partial
     need = wsb(2, 1, 16, 64, 0, 0)
-    assert sp(0x3000, ctypes.byref(_kv()), None, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
-    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, None, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
-    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 0, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
-    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.0, 0x5000, need, 0, None) == ARG
-    assert sp(0x3000, ctypes.byref(_kv(rows=None)), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, None) == ARG
-    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need - 1, 0, None) == WS
+    assert sp(0x3000, ctypes.byref(_kv()), None, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, 2, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, None, 64, 2, 1, 16, 0.07, 0x5000, need, 0, 2, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 0, 2, 1, 16, 0.07, 0x5000, need, 0, 2, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.0, 0x5000, need, 0, 2, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv(rows=None)), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, 2, None) == ARG
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need - 1, 0, 2, None) == WS
+    assert sp(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, 0x5000, need, 0, 7, None) == ARG
     sa = m._lib.mla_sparse_decode_attn
     assert sa(0x3000, ctypes.byref(_kv()), 0x1000, 0x2000, 64, 2, 1, 16, 0.07, None, 2, None, 0x5000, need, 0,
               None) == ARG
@@ -239,7 +241,21 @@ def test_prefill_dispatch_and_workspace(m):
 def test_fp8_math_requires_an_fp8_cache(m):
     f = m._lib.mla_decode_partial_fp8
     need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
-    assert f(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, None) == UNSUP   # bf16 cache
-    assert f(None, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need, 0, None) == ARG
-    assert f(0x3000, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0,
+    assert f(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, 2, None) == UNSUP   # bf16 cache
+    assert f(None, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need, 0, 2, None) == ARG
+    assert f(0x3000, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0, 2,
              None) == WS
+
+
+def test_partial_dtype_is_checked(m):
+    """Partials are fp32 (MLA_FP32 = 2) or bf16 (MLA_BF16 = 0); anything else
+    is rejected before any launch, by the scans and by both merges."""
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    dp = m._lib.mla_decode_partial
+    for bad in (1, 3, -1):
+        assert dp(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, bad, None) == ARG
+        assert m._lib.mla_decode_partial_fp8(0x3000, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07,
+                                             0, 0x5000, need, 0, bad, None) == ARG
+        assert m._lib.mla_decode_combine(2, 1, 16, 256, 0, bad, 0x5000, need, 0x2000, 2, None, None) == ARG
+    assert dp(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0, 0, None) == WS
+    assert m._lib.mla_decode_combine(2, 1, 16, 256, 0, 0, 0x5000, need - 1, 0x2000, 2, None, None) == WS

@@ -40,11 +40,12 @@ def test_decode_step_graph_replays_match_eager(mla, kind):
 
     def step():
         mla.absorb_q(q.view(N, H, -1), w_uk, out=q_lat.view(N, H, -1))
+        # bf16 split partials, as in the timed decode step
         if kind == "sparse":
-            mla.sparse_decode_partial(q_lat, cache, sel_idx, sel_count, SCALE, workspace=ws)
+            mla.sparse_decode_partial(q_lat, cache, sel_idx, sel_count, SCALE, workspace=ws, part_dtype=torch.bfloat16)
         else:
-            mla.decode_partial(q_lat, cache, SCALE, False, workspace=ws)
-        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1))
+            mla.decode_partial(q_lat, cache, SCALE, False, workspace=ws, part_dtype=torch.bfloat16)
+        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1), part_dtype=torch.bfloat16)
 
     step()
     torch.cuda.synchronize()

@@ -143,21 +143,24 @@ def test_split_count_invariance_and_determinism(mla, kind):
 
 @pytest.mark.parametrize("kind", ["contig", "tiny", "verify", "verify_h", "paged", "fp8"])
 @pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
-def test_combine_out_equals_separate_steps(mla, kind, o_dtype):
+@pytest.mark.parametrize("part", [torch.float32, torch.bfloat16])
+def test_combine_out_equals_separate_steps(mla, kind, o_dtype, part):
     """The fused merge + projection gives the bits of the merge followed by
-    the projection, with and without writing o_lat and lse."""
+    the projection, with and without writing o_lat and lse, for fp32 and
+    bf16 split partials."""
     w = small(kind)
     inp = W.generate(w)
     q, w_uk, w_uv, cache = W.to_torch(inp)
     B, s_q, H = w.B, w.s_q, w.H
     q_lat = mla.absorb_q(q.view(B * s_q, H, -1), w_uk).view(B, s_q, H, -1)
-    ws = mla.decode_partial(q_lat, cache, SCALE, w.causal)
+    ws = mla.decode_partial(q_lat, cache, SCALE, w.causal, part_dtype=part)
     lse1 = torch.empty((B, s_q, H), dtype=torch.float32, device=q.device)
-    o1, _ = mla.decode_combine(ws, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype, lse=lse1)
+    o1, _ = mla.decode_combine(ws, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype, lse=lse1, part_dtype=part)
     out1 = mla.absorb_out(o1.view(B * s_q, H, -1), w_uv)
     o2, lse2 = torch.full_like(o1, float("nan")), torch.full_like(lse1, float("nan"))
-    out2 = mla.decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype, o_lat=o2, lse=lse2)
-    out3 = mla.decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype)
+    out2 = mla.decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype, o_lat=o2, lse=lse2,
+                                  part_dtype=part)
+    out3 = mla.decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, o_dtype=o_dtype, part_dtype=part)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(_bits(out2), _bits(out1))
     np.testing.assert_array_equal(_bits(out3), _bits(out1))
