@@ -49,9 +49,19 @@ constexpr int LOADS_PER_WAVE = KT / 4 * CHUNKS / 64;  // 18: each wave loads 16 
 constexpr float REF_STEP = 64.0f;             // reference moves in steps of 2^64
 static_assert(2 * TILE_BYTES + P_BYTES <= 160 * 1024, "LDS budget");
 
+// XOR pattern of the 16-byte chunk index (low 3 bits) of tile row t.  A
+// 128-bit LDS read is served 16 lanes per pass from 64 banks (256 bytes); a
+// score-fragment read puts 16 consecutive tile rows, 1152 bytes apart (128
+// mod 256), in one pass, so rows of equal parity in any aligned run of 16
+// need distinct XORs: bit 1 of t selects bit 2 of the XOR and bits 2..3 of
+// t its bits 0..1.  The transposed value reads (4 consecutive rows x 32
+// bytes) stay conflict-free: rows 4q and 4q + 2 differ in XOR bit 2.
+// tile_swz(t + 16) = tile_swz(t) and tile_swz(t + 8) = tile_swz(t) ^ 2.
+__device__ __forceinline__ int tile_swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+
 __device__ __forceinline__ int lds_off(int t, int elem) {
   const int c = elem >> 3;
-  return (t * CHUNKS + (c ^ chunk_swz(t))) * 16 + (elem & 7) * 2;
+  return (t * CHUNKS + (c ^ tile_swz(t))) * 16 + (elem & 7) * 2;
 }
 
 // floor(a / b) for 0 <= a < 2^62, 0 < b: a double estimate corrected with
@@ -213,16 +223,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 
   // ---- tile loader.  Wave w copies rows 16w..16w+15 of the tile: 18 loads
   // of 64 lanes x 16 B, each filling 1 KB of LDS in order.  The chunk that
-  // lane l fetches for LDS slot 64 k + l follows the XOR swizzle; the pattern
-  // repeats every 8 rows (9 loads), so 9 per-lane byte offsets (< 2^14,
-  // packed two per register) cover all 18 loads.  The buffer window of a tile
-  // ends at the sequence's last row, so rows past it read as zero.
-  uint32_t loff[5] = {0, 0, 0, 0, 0};
+  // lane l fetches for LDS slot 64 k + l follows the XOR swizzle.  Loads k
+  // and k + 9 cover the same slots of rows 8 apart (9 loads fill 8 rows), whose
+  // XORs differ by 2, so 18 per-lane byte offsets within an 8-row group (<
+  // 2^14, packed two per register) cover all loads; the second group's 8-row
+  // displacement is an immediate.  The buffer window of a tile ends at the
+  // sequence's last row, so rows past it read as zero.
+  uint32_t loff[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-  for (int k = 0; k < 9; ++k) {
-    const int s = 64 * k + lane;
+  for (int k = 0; k < 18; ++k) {
+    const int s = 64 * (k % 9) + lane;
     const int tl = s / CHUNKS;
-    const int c = (s - tl * CHUNKS) ^ chunk_swz(tl);
+    const int c = (s - tl * CHUNKS) ^ tile_swz(tl + (k >= 9 ? 8 : 0));
     loff[k >> 1] |= (uint32_t)(tl * ROWW * 2 + c * 16) << (16 * (k & 1));
   }
   const char* rows = (const char*)p.rows;
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0, 0);
     } else {
       constexpr int k9 = k % 9;
-      const uint32_t vo = (loff[k9 >> 1] >> (16 * (k9 & 1))) & 0xFFFFu;
+      const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
       char* dst = smem + buf * TILE_BYTES + wave * (16 * ROWW * 2) + k * 1024;
       if constexpr (SPARSE) {
         // load k covers pattern rows a and a + 1 (lanes from `split` on)
@@ -335,25 +347,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   // 36 k-steps (the rest is an immediate offset)
   uint32_t qoff[4];
   {
-    const int sw = chunk_swz(l32);
+    const int sw = tile_swz(l32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) qoff[i] = l32 * (CHUNKS * 16) + 16 * ((2 * i + half) ^ sw);
   }
   // value-phase transposed-read geometry: lane reads row 16 kap + 4 half +
   // rsel (+8), columns 128 wave + 32 cb + 16 grp + csel; the XOR pattern of
-  // that row is lane-constant and only the parity of cb changes the swizzled
-  // chunk, so two lane offsets cover every read
-  uint32_t pvoff[2];
+  // that row is lane-constant (the +8 row's differs by 2) and only the parity
+  // of cb changes the swizzled chunk, so four lane offsets cover every read
+  uint32_t pvoff[2][2];   // [row + 8][cb parity]
   {
     const int grp = (lane >> 4) & 1;
     const int rsel = (lane & 15) >> 2;
     const int csel = 4 * (lane & 3);
     const int trow = 4 * half + rsel;
-    const int sw = chunk_swz(trow);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int chunk = 16 * wave + 4 * i + 2 * grp + (csel >> 3);
-      pvoff[i] = trow * (CHUNKS * 16) + 16 * (chunk ^ sw) + (csel & 7) * 2;
+    for (int r8 = 0; r8 < 2; ++r8) {
+      const int sw = tile_swz(trow + 8 * r8);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int chunk = 16 * wave + 4 * i + 2 * grp + (csel >> 3);
+        pvoff[r8][i] = trow * (CHUNKS * 16) + 16 * (chunk ^ sw) + (csel & 7) * 2;
+      }
     }
   }
   const uint32_t pb_lane = pbuf_a + lane * 16;
@@ -506,17 +521,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     // (issued two units ahead), B in two buffers (issued at unit cb = 2 of the
     // previous kap); every wait names the exact number of younger LDS reads.
     {
-      const uint32_t pa0 = tb_a + pvoff[0];
-      const uint32_t pa1 = tb_a + pvoff[1];
+      const uint32_t pa0 = tb_a + pvoff[0][0];
+      const uint32_t pa1 = tb_a + pvoff[0][1];
+      const uint32_t pa0_8 = tb_a + pvoff[1][0];
+      const uint32_t pa1_8 = tb_a + pvoff[1][1];
       i16x8 bq[2][4];
       i16x4 tr[3][2];
       auto issue_a = [&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int kap = u >> 2, cb = u & 3;
         constexpr int off = 16 * kap * (CHUNKS * 16) + 128 * (cb >> 1);
-        const uint32_t a = (cb & 1) ? pa1 : pa0;
-        lds_read_tr16<off>(tr[u % 3][0], a);
-        lds_read_tr16<off + 8 * CHUNKS * 16>(tr[u % 3][1], a);
+        lds_read_tr16<off>(tr[u % 3][0], (cb & 1) ? pa1 : pa0);
+        lds_read_tr16<off + 8 * CHUNKS * 16>(tr[u % 3][1], (cb & 1) ? pa1_8 : pa0_8);
       };
       auto issue_b = [&](auto kc) {
         constexpr int kap = decltype(kc)::value;
