@@ -274,20 +274,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
   }
 
   // ---- direct-to-LDS tile loads.  Region rows hold R chunks of 16 B (R = 16
-  // for K_nope and V, 8 for the rope key) with the chunk index XOR-swizzled by
-  // chunk_swz(row); a 1 KB load k fills slots 64 k + lane, so lane l fetches
-  // the chunk that lands there.
+  // for K_nope and V, 8 for the rope key) with the chunk index XORed by a
+  // per-row pattern; a 1 KB load k fills slots 64 k + lane, so lane l fetches
+  // the chunk that lands there.  A 128-bit LDS read is served 16 lanes per
+  // pass from 64 banks (256 B) and a 64-bit transposed read 32 lanes per pass,
+  // so the patterns make those lane groups hit distinct bank slots:
+  //   K_nope (256 B rows; score reads, 16 rows x 1 chunk): chunk ^ (t & 15)
+  //   rope   (128 B rows; score reads):                   chunk ^ ((t >> 1) & 7)
+  //   V      (256 B rows; transposed reads, 4 rows x 4 chunks): chunk ^ 4 (t & 3)
+  // All three are unchanged by t + 32 (and V's by t + 8), which the reads
+  // reach through immediate offsets.
   const int64_t bh = (int64_t)b * H + h;
   const char* kn_base = (const char*)(p.k_nope + bh * p.T_pad * D_NOPE);
   const char* v_base = (const char*)(p.v + bh * p.T_pad * D_V);
   const char* r_base = (const char*)(p.rope + (int64_t)b * p.T_pad * D_ROPE);
-  uint32_t off16[2];
+  // K_nope load 4 w + i covers rows 16 w + 4 i + (lane >> 4); V the same rows;
+  // rope load 2 w + i rows 16 w + 8 i + (lane >> 3)
+  uint32_t offk[4], offr[2];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int t = 4 * k + (lane >> 4);
-    off16[k] = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ chunk_swz(t)));
-  }
-  const uint32_t off8 = (uint32_t)((lane >> 3) * 128 + 16 * ((lane & 7) ^ chunk_swz(lane >> 3)));
+  for (int i = 0; i < 4; ++i)
+    offk[i] = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ ((4 * i + (lane >> 4)) & 15)));
+  const uint32_t offv = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (4 * (lane >> 4))));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) offr[i] = (uint32_t)((lane >> 3) * 128 + 16 * ((lane & 7) ^ (4 * i + (lane >> 4))));
   auto issue_tile = [&](int tile, int buf) {
     const int64_t r0 = (int64_t)tile * KT;
     const auto kn = __builtin_amdgcn_make_buffer_rsrc((void*)(kn_base + r0 * 256), (short)0, KN_BYTES, 0x00020000);
@@ -298,38 +307,37 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 4 * wave + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kn, (lds_void_t*)(dst + k * 1024), 16, off16[i & 1], k * 1024, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vv, (lds_void_t*)(dst + KN_BYTES + KR_BYTES + k * 1024), 16,
-                                               off16[i & 1], k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kn, (lds_void_t*)(dst + k * 1024), 16, offk[i], k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vv, (lds_void_t*)(dst + KN_BYTES + KR_BYTES + k * 1024), 16, offv,
+                                               k * 1024, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int k = 2 * wave + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + KN_BYTES + k * 1024), 16, off8, k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(dst + KN_BYTES + k * 1024), 16, offr[i], k * 1024, 0,
+                                               0);
     }
   };
 
-  // score-phase reads: row l32 (+32), chunk 2 ks + half, XOR-swizzled
-  const int sw = chunk_swz(l32);
-  uint32_t qo_n[4], qo_r[4];
+  // score-phase reads: row l32 (+32), chunk 2 ks + half (k-steps 0..7 in
+  // K_nope, 8..11 in the rope key), XOR-swizzled
+  uint32_t qo_n[8], qo_r[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    qo_n[i] = l32 * 256 + 16 * ((2 * i + half) ^ sw);
-    qo_r[i] = KN_BYTES + l32 * 128 + 16 * ((2 * i + half) ^ sw);
-  }
+  for (int ks = 0; ks < 8; ++ks) qo_n[ks] = l32 * 256 + 16 * ((2 * ks + half) ^ (l32 & 15));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qo_r[i] = KN_BYTES + l32 * 128 + 16 * ((2 * i + half) ^ ((l32 >> 1) & 7));
   // value-phase transposed reads (V^T fragments): lane reads row 16 kap + 4
   // half + rsel (+ 8), columns 32 cb + 16 grp + csel
-  uint32_t pvo[2];
+  uint32_t pvo[4];
   {
     const int grp = (lane >> 4) & 1;
     const int rsel = (lane & 15) >> 2;
     const int csel = 4 * (lane & 3);
     const int trow = 4 * half + rsel;
-    const int s2 = chunk_swz(trow);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int chunk = 4 * i + 2 * grp + (csel >> 3);
-      pvo[i] = KN_BYTES + KR_BYTES + trow * 256 + 16 * (chunk ^ s2) + (csel & 7) * 2;
+    for (int cb = 0; cb < 4; ++cb) {
+      const int chunk = 4 * cb + 2 * grp + (csel >> 3);
+      pvo[cb] = KN_BYTES + KR_BYTES + trow * 256 + 16 * (chunk ^ (4 * rsel)) + (csel & 7) * 2;
     }
   }
 
@@ -352,20 +360,19 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
     // compiler would otherwise wait for the next tile's loads before them)
     f32x16 s0 = {}, s1 = {};
     {
-      uint32_t an[4], ar[4];
+      uint32_t an[8], ar[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        an[i] = tb + qo_n[i];
-        ar[i] = tb + qo_r[i];
-      }
+      for (int i = 0; i < 8; ++i) an[i] = tb + qo_n[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ar[i] = tb + qo_r[i];
       constexpr int QK_AHEAD = 3;
       i16x8 ra[QK_AHEAD + 1][2];
       auto issue_qk = [&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
         constexpr int slot = ks % (QK_AHEAD + 1);
         if constexpr (ks < 8) {
-          lds_read_b128<128 * (ks >> 2)>(ra[slot][0], an[ks & 3]);
-          lds_read_b128<128 * (ks >> 2) + 32 * 256>(ra[slot][1], an[ks & 3]);
+          lds_read_b128<0>(ra[slot][0], an[ks]);
+          lds_read_b128<32 * 256>(ra[slot][1], an[ks]);
         } else {
           lds_read_b128<0>(ra[slot][0], ar[ks & 3]);
           lds_read_b128<32 * 128>(ra[slot][1], ar[ks & 3]);
@@ -384,13 +391,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
       });
     }
     // the first two V^T fragments only need the tile: start them now
-    const uint32_t pv0 = tb + pvo[0], pv1 = tb + pvo[1];
+    uint32_t pv[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) pv[cb] = tb + pvo[cb];
     i16x4 tr[3][2];
     auto issue_a = [&](auto uc) {
       constexpr int u = decltype(uc)::value;
       constexpr int kap = u >> 2, cb = u & 3;
-      constexpr int off = 16 * kap * 256 + 128 * (cb >> 1);
-      const uint32_t a = (cb & 1) ? pv1 : pv0;
+      constexpr int off = 16 * kap * 256;
+      const uint32_t a = pv[cb];
       lds_read_tr16<off>(tr[u % 3][0], a);
       lds_read_tr16<off + 8 * 256>(tr[u % 3][1], a);
     };
