@@ -23,10 +23,11 @@
 //
 // LDS tile layout: 64 rows x 36 chunks of 16 B (576 B rows), written by
 // direct loads with the chunk index XOR-swizzled per row so that both the
-// score reads (32 B of one row per lane, 8 rows per LDS cycle) and the
-// transposed 8-bit reads of the value product (ds_read_b64_tr_b8: 16 lanes
-// read one 16-B chunk from each of 8 rows) hit distinct banks.  A 576-byte
-// row shifts odd rows by half a 128-byte bank line; the swizzle compensates.
+// score reads (128-bit reads, 16 lanes = 16 rows per pass over 64 banks of
+// 256 B) and the transposed 8-bit reads of the value product
+// (ds_read_b64_tr_b8: 32 lanes per pass read 2 chunks of rows b .. b + 3 and
+// b + 8 .. b + 11) hit distinct banks.  A 576-byte row starts 64 B further
+// into the 256-byte bank row than the one before; the swizzle compensates.
 #include "mla_common.h"
 #include "mla_internal.h"
 #include "mla_plan.h"
@@ -48,15 +49,13 @@ constexpr int E_NONE = -100000;                // no scale seen yet
 static_assert(PB_BYTES >= PLAN_SCRATCH_BYTES, "plan scratch");
 static_assert(2 * STAGE + PB_BYTES + 2 * SC_BYTES <= 160 * 1024, "LDS budget");
 
-// chunk XOR pattern of tile row t (t & 15 matters): bank group of (row t,
-// physical chunk) is chunk ^ 4 (t & 1) (mod 8, 16-B groups of a 128-B line),
-// so the pattern f(t) ^ 4 (t & 1) makes the bank group of logical chunk c
-// c ^ f(t), with f distinct over any 8 consecutive rows and over rows
-// {r .. r + 3, r + 8 .. r + 11} (r = 0, 4 mod 16)
-__device__ __forceinline__ int f8_swz(int t) {
-  const int f = (t & 7) ^ (((t >> 3) & 1) << 2);
-  return f ^ ((t & 1) << 2);
-}
+// chunk XOR pattern of tile row t: the 16-byte bank slot of (row t, physical
+// chunk p) is 4 (t & 3) + p (mod 16), so rows t .. t + 3 already fall in
+// different quarters and the XOR (t >> 2) & 3 separates the four such groups
+// of an aligned run of 16 rows (score reads); for the transposed reads rows
+// b .. b + 3 and b + 8 .. b + 11 differ in XOR bit 1.  Period 16, so row
+// offsets of 16 and 32 are immediates.
+__device__ __forceinline__ int f8_swz(int t) { return (t >> 2) & 3; }
 // logical -> physical chunk of row t (an involution per row); the four rope
 // chunks 32..35 stay among themselves
 __device__ __forceinline__ int f8_chunk(int t, int c) {
