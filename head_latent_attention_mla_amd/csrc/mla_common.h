@@ -61,6 +61,17 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& c0, f32x16& c1) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c0), "+v"(c1));
 }
 
+// XOR pattern of the 16-byte chunk index (low 3 bits) of a bf16 latent-cache
+// tile row t (tiles stored row-major, 1152 bytes per row).  A
+// 128-bit LDS read is served 16 lanes per pass from 64 banks (256 bytes); a
+// score-fragment read puts 16 consecutive tile rows, 1152 bytes apart (128
+// mod 256), in one pass, so rows of equal parity in any aligned run of 16
+// need distinct XORs: bit 1 of t selects bit 2 of the XOR and bits 2..3 of
+// t its bits 0..1.  The transposed value reads (4 consecutive rows x 32
+// bytes) stay conflict-free: rows 4q and 4q + 2 differ in XOR bit 2.
+// tile_swz(t + 16) = tile_swz(t) and tile_swz(t + 8) = tile_swz(t) ^ 2.
+__device__ __forceinline__ int tile_swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+
 // Compile-time loop: f(std::integral_constant<int, I>{}) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -133,9 +144,10 @@ __device__ __forceinline__ f32x4 part_vals(PartRaw<PB16> r) {
   }
 }
 
+// (two v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint64_t pack_bf16x4(f32x4 v) {
-  return (uint64_t)bf16_bits(to_bf16(v[0])) | ((uint64_t)bf16_bits(to_bf16(v[1])) << 16) |
-         ((uint64_t)bf16_bits(to_bf16(v[2])) << 32) | ((uint64_t)bf16_bits(to_bf16(v[3])) << 48);
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint64_t, __builtin_convertvector(v, bf16x4_t));
 }
 
 __device__ __forceinline__ void part_store(void* base, int64_t elem, f32x4 v, bool pb16) {

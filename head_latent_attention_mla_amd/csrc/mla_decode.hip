@@ -35,6 +35,7 @@
 // parts of each sequence.
 #include "mla_common.h"
 #include "mla_internal.h"
+#include "mla_split_store.h"
 
 namespace mla {
 
@@ -48,16 +49,7 @@ constexpr int NTHREADS = 256;
 constexpr int LOADS_PER_WAVE = KT / 4 * CHUNKS / 64;  // 18: each wave loads 16 rows
 constexpr float REF_STEP = 64.0f;             // reference moves in steps of 2^64
 static_assert(2 * TILE_BYTES + P_BYTES <= 160 * 1024, "LDS budget");
-
-// XOR pattern of the 16-byte chunk index (low 3 bits) of tile row t.  A
-// 128-bit LDS read is served 16 lanes per pass from 64 banks (256 bytes); a
-// score-fragment read puts 16 consecutive tile rows, 1152 bytes apart (128
-// mod 256), in one pass, so rows of equal parity in any aligned run of 16
-// need distinct XORs: bit 1 of t selects bit 2 of the XOR and bits 2..3 of
-// t its bits 0..1.  The transposed value reads (4 consecutive rows x 32
-// bytes) stay conflict-free: rows 4q and 4q + 2 differ in XOR bit 2.
-// tile_swz(t + 16) = tile_swz(t) and tile_swz(t + 8) = tile_swz(t) ^ 2.
-__device__ __forceinline__ int tile_swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
+static_assert(SPLIT_STAGE_BYTES <= 2 * TILE_BYTES, "partial staging fits the tile buffers");
 
 __device__ __forceinline__ int lds_off(int t, int elem) {
   const int c = elem >> 3;
@@ -597,33 +589,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     }
   }
 
-  // ---- epilogue: share each row's normaliser, write the normalised partials
-  barrier_lds();
+  // ---- epilogue: share each row's normaliser, write the normalised partials.
+  // The partials are staged over the tile buffers: the loads issued past the
+  // last tile must have landed first.
+  barrier_tile_ready();
   float* const lsh = (float*)pbuf;          // [128] l_sum
   if (half == 0) lsh[wave * 32 + l32] = l_sum;
   barrier_lds();
 
-  // partial rows are row-major [slot][R][512], slot = k + b (unique: along
-  // the plan, k and b never both stay put); a lane pair covers 128
-  // contiguous bytes of one row per (cb, rb) (64 as bf16), stored back to back
+  // the tile buffers are idle: the partial rows are staged there
   const int64_t pbase = (int64_t)sl * p.R;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = g * 128 + rb * 32 + l32;
-    if (row >= p.R) continue;
-    const float l = lsh[rb * 32 + l32];
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t prow = (pbase + row) * D_C + wave * 128 + 4 * half;   // element index
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = {acc[cb][rb][4 * q4] * inv, acc[cb][rb][4 * q4 + 1] * inv,
-                         acc[cb][rb][4 * q4 + 2] * inv, acc[cb][rb][4 * q4 + 3] * inv};
-        part_store(p.part_o, prow + cb * 32 + 8 * q4, v, p.part_bf16 != 0);
-      }
-    }
-  }
+  store_split_partials(p, acc, lsh, smem, pbase, g, wave, lane);
   if (half == 0 && own_ok) p.part_lse[pbase + own_r] = l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
 }
 

@@ -30,6 +30,7 @@
 // into the 256-byte bank row than the one before; the swizzle compensates.
 #include "mla_common.h"
 #include "mla_internal.h"
+#include "mla_split_store.h"
 #include "mla_plan.h"
 
 namespace mla {
@@ -47,7 +48,11 @@ constexpr int SC_BYTES = 2 * KT * 4;           // row scales of one tile and the
 constexpr float REF_STEP = 8.0f;               // probabilities stay <= 2^8 (E4M3 max 448)
 constexpr int E_NONE = -100000;                // no scale seen yet
 static_assert(PB_BYTES >= PLAN_SCRATCH_BYTES, "plan scratch");
-static_assert(2 * STAGE + PB_BYTES + 2 * SC_BYTES <= 160 * 1024, "LDS budget");
+constexpr int MAIN_BYTES = 2 * STAGE + PB_BYTES + 2 * SC_BYTES;
+// the partial rows are staged over the whole buffer at the end, with the
+// row normalisers past them
+constexpr int SMEM_BYTES = MAIN_BYTES > SPLIT_STAGE_BYTES + 512 ? MAIN_BYTES : SPLIT_STAGE_BYTES + 512;
+static_assert(SMEM_BYTES <= 160 * 1024, "LDS budget");
 
 // chunk XOR pattern of tile row t: the 16-byte bank slot of (row t, physical
 // chunk p) is 4 (t & 3) + p (mod 16), so rows t .. t + 3 already fall in
@@ -81,7 +86,7 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 
 template <bool PAGED>
 __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + PB_BYTES + 2 * SC_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM_BYTES];
   char* const pbuf = smem + 2 * STAGE;
   float* const scl = (float*)(smem + 2 * STAGE + PB_BYTES);   // per buffer: 64 scales, then 64 reciprocals
   const uint32_t smem_a = lds_addr(smem);
@@ -431,30 +436,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     }
   }
 
-  // ---- epilogue: share each row's normaliser, write the normalised partials
-  barrier_lds();
-  float* const lsh = (float*)pbuf;          // [128] l_sum
+  // ---- epilogue: share each row's normaliser, write the normalised partials.
+  // The partials are staged over the tile buffers: the loads issued past the
+  // last tile must have landed first.
+  barrier_tile_ready();
+  float* const lsh = (float*)(smem + SPLIT_STAGE_BYTES);   // [128] l_sum
   if (half == 0) lsh[wave * 32 + l32] = l_sum;
   barrier_lds();
   const float unscale = e_cur == E_NONE ? 1.0f : __builtin_ldexpf(1.0f, e_cur);
   const int64_t pbase = (int64_t)sl * p.R;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int row = g * 128 + rb * 32 + l32;
-    if (row >= p.R) continue;
-    const float l = lsh[rb * 32 + l32];
-    const float inv = l > 0.f ? unscale / l : 0.f;
-    const int64_t prow = (pbase + row) * D_C + wave * 128 + 4 * half;   // element index
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = {acc[cb][rb][4 * q4] * inv, acc[cb][rb][4 * q4 + 1] * inv,
-                         acc[cb][rb][4 * q4 + 2] * inv, acc[cb][rb][4 * q4 + 3] * inv};
-        part_store(p.part_o, prow + cb * 32 + 8 * q4, v, p.part_bf16 != 0);
-      }
-    }
-  }
+  store_split_partials(p, acc, lsh, smem, pbase, g, wave, lane, unscale);
   if (half == 0 && own_ok) p.part_lse[pbase + own_r] = l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
 }
 
