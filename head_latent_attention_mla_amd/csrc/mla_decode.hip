@@ -365,9 +365,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   }
   const uint32_t pb_lane = pbuf_a + lane * 16;
 
-  // zero both tile buffers once (LDS of rows past a sequence end stays finite)
-  for (int i = tid; i < 2 * TILE_BYTES / 16; i += NTHREADS) ((i16x8*)smem)[i] = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  barrier_lds();
+  // No clearing of the tile buffers is needed: every tile row the loop reads
+  // was written by the loads (rows outside a tile's window load as zeros) or,
+  // for FP8 caches, by the conversion of all 64 staged rows.
 
   float sc_cur = 0.f, sc_next = 0.f;            // FP8 row scales (this tile, next)
   if (n_tiles > 0) {
