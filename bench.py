@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 # holds only for the code it was taken on
 KERNEL_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_decode.hip",
                   "head_latent_attention_mla_amd/csrc/mla_common.h",
-                  "head_latent_attention_mla_amd/csrc/mla_internal.h")
+                  "head_latent_attention_mla_amd/csrc/mla_internal.h",
+                  "head_latent_attention_mla_amd/csrc/mla_split_store.h")
 COPY_BYTES = 1 << 30         # read (and written) by the copy-kernel calibration run
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
