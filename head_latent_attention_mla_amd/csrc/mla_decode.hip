@@ -251,19 +251,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   };
   // SPARSE: row offsets of this wave's 16 tile rows, relative to the loader's
   // 8-row pattern (adj[r] + the pattern offset = position * 1152 + chunk);
-  // rows past the selection or outside the sequence point past the window
+  // rows past the selection or outside the sequence point past the window.
+  // The selected positions are fetched one tile ahead of their use, with a
+  // vector load (lane l < 16 -> row 16 wave + l), so the wait for them is
+  // the tile loads' own.
   constexpr uint32_t OOB = 0x40000000u;
   uint32_t adj[16];
-  auto set_rows = [&](int tile) {
+  int sel_v = -1;
+  auto fetch_rows = [&](int tile) {
     if constexpr (SPARSE) {
-      const int r0 = t_begin + tile * KT + 16 * wave;
-      const int32_t* ip = p.sel_idx + (int64_t)b * p.k_max + r0;
-      const int src = p.src_len[b];
+      const int t = t_begin + tile * KT + 16 * wave + (lane & 15);
+      sel_v = t < T ? p.sel_idx[(int64_t)b * p.k_max + t] : -1;
+    }
+  };
+  const int src_b = SPARSE ? p.src_len[b] : 0;
+  auto set_rows = [&]() {
+    if constexpr (SPARSE) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int pos = r0 + r < T ? ip[r] : -1;
-        const uint32_t a = (pos >= 0 && pos < src) ? (uint32_t)(pos - (r & 7)) * (ROWW * 2) : OOB;
-        adj[r] = __builtin_amdgcn_readfirstlane(a);
+        const int pos = __builtin_amdgcn_readlane(sel_v, r);
+        const uint32_t a = (pos >= 0 && pos < src_b) ? (uint32_t)(pos - (r & 7)) * (ROWW * 2) : OOB;
+        adj[r] = __builtin_amdgcn_readfirstlane(a);   // keep the offsets in scalar registers
       }
     }
   };
@@ -371,8 +379,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 
   float sc_cur = 0.f, sc_next = 0.f;            // FP8 row scales (this tile, next)
   if (n_tiles > 0) {
-    set_rows(0);
+    fetch_rows(0);
+    set_rows();
     issue_tile(0, 0);
+    fetch_rows(1);
     if constexpr (FP8) sc_next = load_scale(0);
   }
 
@@ -382,7 +392,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     // past the last tile the loads still run (no branch in the loop) but
     // read an empty window into the idle buffer
     const auto next = tile_rsrc(has_next ? tile + 1 : tile, has_next);
-    if constexpr (SPARSE) set_rows(has_next ? tile + 1 : tile);
+    if constexpr (SPARSE) {
+      // positions of tile + 1 (landed with the tile); past the last tile the
+      // window is empty and the offsets do not matter
+      set_rows();
+      fetch_rows(tile + 2);
+    }
     const int next_buf = (tile + 1) & 1;
     uint32_t tb_a;
     if constexpr (FP8) {
@@ -405,7 +420,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       uint32_t qa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) qa[i] = tb_a + qoff[i];
-      constexpr int QK_AHEAD = 3;              // k-steps of A fragments in flight
+      // k-steps of A fragments in flight (the sparse variant gives one up for
+      // the prefetched positions)
+      constexpr int QK_AHEAD = SPARSE ? 2 : 3;
       i16x8 ra[QK_AHEAD + 1][2];
       auto issue_qk = [&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
