@@ -97,13 +97,13 @@ struct PrefillLayout {
 };
 
 // Workspace of the expand path: W_UV^T per head, then K_nope and V
-// [B, H, T_pad, 128] (T_pad: max_seqlen rounded up to 128) and the rope keys [B, T_pad, 64] (bf16), 256-aligned.
+// [B, T_pad, H * 128 + 64] (token-major; T_pad: max_seqlen rounded up to 128) and the rope keys [B, T_pad, 64] (bf16), 256-aligned.
 bool prefill_layout(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, PrefillLayout* l) {
   if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || s_q > max_seqlen) return false;
   if (B > (1 << 16) || H > (1 << 12) || max_seqlen > (1 << 24)) return false;
   if ((int64_t)B * s_q * H > (1 << 30)) return false;
   l->T_pad = (int32_t)((max_seqlen + 127) / 128 * 128);
-  const size_t kv = (size_t)B * H * l->T_pad * mla::D_NOPE * sizeof(uint16_t);
+  const size_t kv = (size_t)B * l->T_pad * mla::prefill_kv_ld(H) * sizeof(uint16_t);
   l->wuvt_off = 0;
   l->kn_off = align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t));
   l->v_off = l->kn_off + align_up(kv);
@@ -154,6 +154,7 @@ mla_status prefill_impl(const void* q, const mla_kv_desc* kv, const void* w_uk, 
   p.s_q = s_q;
   p.H = H;
   p.T_pad = l.T_pad;
+  p.kv_ld = (int32_t)mla::prefill_kv_ld(H);
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.causal = causal;
   p.fp8 = kv->dtype == MLA_FP8_E4M3;

@@ -103,6 +103,11 @@ struct AppendParams {
 
 // One call of the expand (prefill) path: expand every cached row per head
 // into K_nope and V, then causal flash attention with the 192-wide queries.
+// Token rows of the expanded keys and values hold the H heads' 128 values
+// and 64 elements of padding, so that the rows of one head are not a power
+// of two apart (those map a tile's rows onto few cache sets and channels).
+inline int64_t prefill_kv_ld(int64_t H) { return H * D_NOPE + 64; }
+
 struct PrefillParams {
   const uint16_t* q;            // bf16 [B, s_q, H, 192]
   const void* rows;             // cache rows (contiguous or pool), bf16 or e4m3
@@ -112,19 +117,26 @@ struct PrefillParams {
   const uint16_t* w_uk;         // bf16 [H, 128, 512]
   const uint16_t* w_uv;         // bf16 [H, 512, 128]
   uint16_t* w_uvt;              // workspace: bf16 [H, 128, 512], W_UV per head transposed
-  uint16_t* k_nope;             // workspace: bf16 [B, H, T_pad, 128]
-  uint16_t* v;                  // workspace: bf16 [B, H, T_pad, 128]
+  uint16_t* k_nope;             // workspace: bf16 [B, T_pad, kv_ld] (token-major, head h at h * 128)
+  uint16_t* v;                  // workspace: bf16 [B, T_pad, kv_ld] (token-major, head h at h * 128)
   uint16_t* rope;               // workspace: bf16 [B, T_pad, 64]
   uint16_t* out;                // bf16 [B, s_q, H, 128]
   int64_t T_stride;
   int32_t max_blocks;
   int32_t B, s_q, H;
   int32_t T_pad;                // rows per sequence in the expanded buffers (multiple of 128)
+  int32_t kv_ld;                // elements per token row of K_nope and V: H * 128 + 64
   float scale_log2;
   int32_t causal;
   int32_t fp8;
 };
 
+// Column-major C (M x N, ldc) = op(A) (M x K) op(B) (K x N) in bf16 with
+// fp32 accumulation, through hipBLASLt (mla_gemm.cpp); batch products with
+// the given element strides between consecutive A, B and C (0: shared).
+hipError_t gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                     const void* B, int64_t ldb, void* C, int64_t ldc, int batch, int64_t stride_a,
+                     int64_t stride_b, int64_t stride_c, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);

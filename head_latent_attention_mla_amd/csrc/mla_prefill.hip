@@ -4,12 +4,18 @@
 // narrower per-pair contraction wins; "MLA, dim by dim", "MLA Prefill": form
 // K = C W_UK and V = C W_UV once, then run ordinary attention over them).
 //
-// Two kernels:
-//   expand_kv_kernel   one persistent work-group per (head, K or V) holds that
-//       half of the head's weights in LDS and streams every cached row
-//       through MFMA: K_nope^T and V^T tiles rounded to bf16 into
-//       [B, H, T_pad, 128] (rows past a sequence's end written as 0);
-//       copy_rope_kernel copies the rows' rope keys to [B, T_pad, 64].
+// The expansion writes K_nope and V token-major, [B, T_pad, H * 128 + 64]
+// bf16 (head h at h * 128 of a row; the pad keeps one head's rows from being
+// a power of two apart):
+//   contiguous bf16 caches: per sequence two plain matrix products over all
+//       heads at once (hipBLASLt), K = C W_UK^T and V = C W_UV;
+//   FP8 or paged caches: expand_kv_kernel, one persistent work-group per
+//       (head, K or V) that holds that half of the head's weights in LDS and
+//       streams every cached row (dequantised, gathered) through MFMA, rows
+//       past a sequence's end written as 0.
+//   copy_rope_kernel copies the rows' rope keys to [B, T_pad, 64].
+// Rows past a sequence's end are masked in the attention (they may hold
+// anything on the first route).  Then one attention kernel:
 //   prefill_attn_kernel  per (128 query rows, head, sequence): causal flash
 //       attention.  Each wave owns 32 query rows: S^T = K Q^T (the K tile from
 //       LDS, the query rows held in registers), an online softmax per row,
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
         // lane holds D[n = 64 nq + 32 nb + 8 g + 4 half + e][t = 64 tq + 32 tb + l32]
         const int b = tile / n_tt, t0 = (tile % n_tt) * ET;
         const int T = p.seqlens[b];
-        uint16_t* dst = (part ? p.v : p.k_nope) + (((int64_t)b * p.H + h) * p.T_pad + t0) * D_NOPE;
+        uint16_t* dst = (part ? p.v : p.k_nope) + ((int64_t)b * p.T_pad + t0) * p.kv_ld + h * D_NOPE;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const int t = 64 * tq + 32 * tb + l32;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[nb][tb][4 * g + e])) << (16 * e);
               }
-              *(uint64_t*)(dst + (int64_t)t * D_NOPE + 64 * nq + 32 * nb + 8 * g + 4 * half) = v;
+              *(uint64_t*)(dst + (int64_t)t * p.kv_ld + 64 * nq + 32 * nb + 8 * g + 4 * half) = v;
             }
             acc[nb][tb] = f32x16{};
           }
@@ -284,32 +290,42 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
   //   V      (256 B rows; transposed reads, 4 rows x 4 chunks): chunk ^ 4 (t & 3)
   // All three are unchanged by t + 32 (and V's by t + 8), which the reads
   // reach through immediate offsets.
-  const int64_t bh = (int64_t)b * H + h;
-  const char* kn_base = (const char*)(p.k_nope + bh * p.T_pad * D_NOPE);
-  const char* v_base = (const char*)(p.v + bh * p.T_pad * D_V);
+  // K_nope and V are token-major [B, T_pad, kv_ld]: the 256-byte rows of
+  // head h are RS = 2 kv_ld bytes apart
+  const int64_t RS = (int64_t)p.kv_ld * 2;
+  const char* kn_base = (const char*)(p.k_nope + (int64_t)b * p.T_pad * p.kv_ld + h * D_NOPE);
+  const char* v_base = (const char*)(p.v + (int64_t)b * p.T_pad * p.kv_ld + h * D_V);
   const char* r_base = (const char*)(p.rope + (int64_t)b * p.T_pad * D_ROPE);
   // K_nope load 4 w + i covers rows 16 w + 4 i + (lane >> 4); V the same rows;
   // rope load 2 w + i rows 16 w + 8 i + (lane >> 3)
-  uint32_t offk[4], offr[2];
+  // The K_nope and V windows of a tile end at the sequence's last row, so
+  // rows past it load as zeros whatever the workspace holds there; the whole
+  // offset of a load sits in its lane offset, which the window bounds.
+  const int T_u = __builtin_amdgcn_readfirstlane(T);   // the windows must be uniform
+  uint32_t offk[4], offv[4], offr[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    offk[i] = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ ((4 * i + (lane >> 4)) & 15)));
-  const uint32_t offv = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (4 * (lane >> 4))));
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t base = (uint32_t)(4 * (4 * wave + i) + (lane >> 4)) * (uint32_t)RS;
+    offk[i] = base + 16 * ((lane & 15) ^ ((4 * i + (lane >> 4)) & 15));
+    offv[i] = base + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) offr[i] = (uint32_t)((lane >> 3) * 128 + 16 * ((lane & 7) ^ (4 * i + (lane >> 4))));
   auto issue_tile = [&](int tile, int buf) {
     const int64_t r0 = (int64_t)tile * KT;
-    const auto kn = __builtin_amdgcn_make_buffer_rsrc((void*)(kn_base + r0 * 256), (short)0, KN_BYTES, 0x00020000);
-    const auto vv = __builtin_amdgcn_make_buffer_rsrc((void*)(v_base + r0 * 256), (short)0, V_BYTES, 0x00020000);
+    const int valid = max(0, min(KT, T_u - (int)r0));
+    const int kv_bytes = valid * (int)RS;
+    const auto kn = __builtin_amdgcn_make_buffer_rsrc((void*)(kn_base + r0 * RS), (short)0, kv_bytes, 0x00020000);
+    const auto vv = __builtin_amdgcn_make_buffer_rsrc((void*)(v_base + r0 * RS), (short)0, kv_bytes, 0x00020000);
     const auto kr = __builtin_amdgcn_make_buffer_rsrc((void*)(r_base + r0 * 128), (short)0, KR_BYTES, 0x00020000);
     char* dst = smem + buf * BUF_BYTES;
     // wave w: K_nope and V loads 4 w .. 4 w + 3, rope loads 2 w, 2 w + 1
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = 4 * wave + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kn, (lds_void_t*)(dst + k * 1024), 16, offk[i], k * 1024, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vv, (lds_void_t*)(dst + KN_BYTES + KR_BYTES + k * 1024), 16, offv,
-                                               k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kn, (lds_void_t*)(dst + k * 1024), 16, offk[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vv, (lds_void_t*)(dst + KN_BYTES + KR_BYTES + k * 1024), 16, offv[i],
+                                               0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -494,12 +510,30 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
   if (e != hipSuccess) return e;
-  if (p.fp8)
-    hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(expand_kv_kernel<false>, dim3(2 * p.H), dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!p.fp8 && p.block_table == nullptr) {
+    // contiguous bf16 rows: per sequence two plain products over all heads at
+    // once, in column-major terms K^T (H*128 x n) = W (H*128 x 512) C^T
+    // (512 x n), with W = W_UK or W_UV^T as [H*128, 512] row-major and C the
+    // rows' latent parts (row pitch 576); K^T lands token-major with leading
+    // dimension kv_ld.  n = the rows the cache holds per sequence, up to T_pad.
+    const int64_t n = min((int64_t)p.T_pad, p.T_stride);
+    const int64_t hd = (int64_t)p.H * D_NOPE;
+    for (int b = 0; b < p.B; ++b) {
+      const uint16_t* c = (const uint16_t*)p.rows + (int64_t)b * p.T_stride * ROWW;
+      const int64_t o = (int64_t)b * p.T_pad * p.kv_ld;
+      e = gemm_bf16(true, false, hd, n, D_C, p.w_uk, D_C, c, ROWW, p.k_nope + o, p.kv_ld, 1, 0, 0, 0, stream);
+      if (e != hipSuccess) return e;
+      e = gemm_bf16(true, false, hd, n, D_C, p.w_uvt, D_C, c, ROWW, p.v + o, p.kv_ld, 1, 0, 0, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    if (p.fp8)
+      hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL(expand_kv_kernel<false>, dim3(2 * p.H), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(copy_rope_kernel, dim3(p.T_pad / ET, p.B), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

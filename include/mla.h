@@ -361,7 +361,7 @@ mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_
  * the value sum accumulate in fp32 on the matrix cores.
  *   q        bf16 [B, s_q, H, 192];  out  bf16 [B, s_q, H, 128]
  *   workspace  ws_bytes >= mla_prefill_workspace_bytes(B, s_q, H, max_seqlen):
- *            W_UV^T, K_nope and V [B, H, T_pad, 128] and the rope keys
+ *            W_UV^T, K_nope and V [B, T_pad, H * 128 + 64] (token-major) and the rope keys
  *            [B, T_pad, 64], T_pad = max_seqlen rounded up to 128.
  * s_q <= max_seqlen; 0 from mla_prefill_workspace_bytes means an invalid size. */
 size_t mla_prefill_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);

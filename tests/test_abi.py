@@ -215,7 +215,10 @@ def test_prefill_dispatch_and_workspace(m):
     assert ue(1, 1) == 1 and ue(0, 5) == -1 and ue(3, 0) == -1
     pw = m._lib.mla_prefill_workspace_bytes
     # T_pad 384: W_UV^T 2 MiB, K_nope and V 2 x 16 x 384 x 128 x 2 B each, rope 2 x 384 x 64 x 2 B
-    assert pw(2, 300, 16, 300) == 2 * 2 ** 20 + 2 * 3 * 2 ** 20 + 98304
+    # W_UV^T (16 x 128 x 512 bf16 = 2 MiB), K_nope and V token-major
+    # [2, T_pad = 384, 16 * 128 + 64] bf16 each, rope keys [2, 384, 64] bf16
+    kv = 2 * 384 * (16 * 128 + 64) * 2
+    assert pw(2, 300, 16, 300) == 2 * 2 ** 20 + 2 * kv + 2 * 384 * 64 * 2
     assert pw(2, 301, 16, 300) == 0 and pw(0, 1, 16, 300) == 0
     aw = m._lib.mla_attend_workspace_bytes
     assert aw(2, 300, 16, 300) == pw(2, 300, 16, 300)                      # expand path
