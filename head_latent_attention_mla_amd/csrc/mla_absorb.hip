@@ -287,12 +287,16 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
   issue_w(0);
   issue_w(1);
 
-  // ---- merge: thread -> row r = tid / TPR, columns 4 (tid % TPR) + 4 TPR i;
-  // fewer rows in the block get more threads each (TPR = 8, 16 or 32)
+  // ---- merge: thread -> row r = tid / TPR, columns VW (tid % TPR) + VW TPR i
+  // (VW = 8 bf16 or 4 fp32 partial values: 16-byte loads, so the TPR threads
+  // of a row read whole 128-byte lines); fewer rows in the block get more
+  // threads each (TPR = 8, 16 or 32)
   auto merge = [&](auto tprc) {
     constexpr int TPR = decltype(tprc)::value;
-    constexpr int NCH = D_C / 4 / TPR;       // 16-byte column chunks per thread
-    const int r = tid / TPR, cq = (tid % TPR) * 4;
+    constexpr int VW = PB16 ? 8 : 4;
+    constexpr int NCH = D_C / VW / TPR;      // 16-byte column chunks per thread
+    using Raw = typename std::conditional<PB16, u32x4, f32x4>::type;
+    const int r = tid / TPR, cq = (tid % TPR) * VW;
     const int n = n0 + r;
     const bool ok = r < CO_ROWS && n < N;
     const int b = ok ? n / s_q : 0;
@@ -304,18 +308,31 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
     // added in split order.  The first group's partials are loaded with the
     // log-sum-exps, before the maximum is known (it only sets their weights).
     constexpr int SG = 4;
-    auto load_group = [&](int s0, float (&l)[SG], PartRaw<PB16> (&d)[SG][NCH]) {
+    auto load_group = [&](int s0, float (&l)[SG], Raw (&d)[SG][NCH]) {
 #pragma unroll
       for (int u = 0; u < SG; ++u) {
         const int s = max(min(s0 + u, n_split - 1), 0);
         l[u] = part_lse[(sb + s) * R + row];
         const int64_t src = ((sb + s) * R + row) * D_C + cq;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) d[u][i] = part_load<PB16>(part_o, src + 4 * TPR * i);
+        for (int i = 0; i < NCH; ++i) {
+          if constexpr (PB16) d[u][i] = *(const u32x4*)((const uint16_t*)part_o + src + VW * TPR * i);
+          else d[u][i] = *(const f32x4*)((const float*)part_o + src + VW * TPR * i);
+        }
+      }
+    };
+    // values 4 j .. 4 j + 3 of a loaded chunk
+    auto vals = [&](const Raw& x, int j) -> f32x4 {
+      if constexpr (PB16) {
+        const uint32_t lo = x[2 * j], hi = x[2 * j + 1];
+        return f32x4{__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                     __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xFFFF0000u)};
+      } else {
+        return x;
       }
     };
     float l[SG];
-    PartRaw<PB16> d[SG][NCH];
+    Raw d[SG][NCH];
     load_group(0, l, d);
     float mx = -INFINITY;
 #pragma unroll
@@ -325,9 +342,11 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
       for (int u = 0; u < SG; ++u) mx = fmaxf(mx, part_lse[(sb + min(s0 + u, n_split - 1)) * R + row]);
     }
     float wsum = 0.f;
-    f32x4 acc[NCH];
+    f32x4 acc[NCH][VW / 4];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int j = 0; j < VW / 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < n_split; s0 += SG) {
       if (s0 > 0) load_group(s0, l, d);
       float w[SG];
@@ -338,34 +357,38 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
         if (w[u] == 0.f) continue;      // absent or empty split: its partial may hold anything
         wsum += w[u];
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) acc[i] += w[u] * part_vals<PB16>(d[u][i]);
+        for (int i = 0; i < NCH; ++i)
+#pragma unroll
+          for (int j = 0; j < VW / 4; ++j) acc[i][j] += w[u] * vals(d[u][i], j);
       }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
     if (r >= CO_ROWS) return;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      f32x4 v = acc[i] * inv;
-      if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int k = cq + 4 * TPR * i;
-      if (ok && o_lat != nullptr) {
-        const int64_t o = ((int64_t)n * H + h) * D_C + k;
-        part_store(o_lat, o, v, o_bf16 != 0);
-      }
-      // the projection sees the latent output at the precision the caller
-      // asked for: bf16 as is, fp32 as high + low bf16 terms
-      uint16_t hi[4], lo[4];
+    for (int i = 0; i < NCH; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const __bf16 bh = to_bf16(v[e]);
-        hi[e] = bf16_bits(bh);
-        lo[e] = o_bf16 ? (uint16_t)0 : bf16_bits(to_bf16(v[e] - (float)bh));
+      for (int j = 0; j < VW / 4; ++j) {
+        f32x4 v = acc[i][j] * inv;
+        if (!ok) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int k = cq + VW * TPR * i + 4 * j;
+        if (ok && o_lat != nullptr) {
+          const int64_t o = ((int64_t)n * H + h) * D_C + k;
+          part_store(o_lat, o, v, o_bf16 != 0);
+        }
+        // the projection sees the latent output at the precision the caller
+        // asked for: bf16 as is, fp32 as high + low bf16 terms
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 bh = to_bf16(v[e]);
+          hi[e] = bf16_bits(bh);
+          lo[e] = o_bf16 ? (uint16_t)0 : bf16_bits(to_bf16(v[e] - (float)bh));
+        }
+        const uint64_t ph = (uint64_t)hi[0] | ((uint64_t)hi[1] << 16) | ((uint64_t)hi[2] << 32) | ((uint64_t)hi[3] << 48);
+        const uint64_t pl = (uint64_t)lo[0] | ((uint64_t)lo[1] << 16) | ((uint64_t)lo[2] << 32) | ((uint64_t)lo[3] << 48);
+        *(uint64_t*)(at[0] + co_aoff(r, k)) = ph;
+        *(uint64_t*)(at[1] + co_aoff(r, k)) = pl;
       }
-      const uint64_t ph = (uint64_t)hi[0] | ((uint64_t)hi[1] << 16) | ((uint64_t)hi[2] << 32) | ((uint64_t)hi[3] << 48);
-      const uint64_t pl = (uint64_t)lo[0] | ((uint64_t)lo[1] << 16) | ((uint64_t)lo[2] << 32) | ((uint64_t)lo[3] << 48);
-      *(uint64_t*)(at[0] + co_aoff(r, k)) = ph;
-      *(uint64_t*)(at[1] + co_aoff(r, k)) = pl;
-    }
     if (ok && lse_out != nullptr && (tid % TPR) == 0)
       lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
   };
