@@ -66,6 +66,9 @@ def small(kind, **kw):
         paged=W.Workload("paged", B=4, H=128, s_q=1, causal=False, T_range=(70, 400), paged=True, seed=33),
         verify=W.Workload("verify", B=2, H=128, s_q=4, causal=True, T=301, seed=44),
         verify_h=W.Workload("verify_h", B=2, H=40, s_q=3, causal=True, T=130, seed=45),
+        # R = 132 query rows per sequence: a second row group of 4 rows (the
+        # partial store writes only the rows that exist)
+        groups_ragged=W.Workload("groups_ragged", B=3, H=66, s_q=2, causal=True, T=150, T_stride=160, seed=46),
         fp8=W.Workload("fp8", B=2, H=128, s_q=2, causal=True, T=333, cache_dtype="fp8", T_stride=350, seed=55),
         fp8_paged=W.Workload("fp8_paged", B=3, H=64, s_q=1, causal=False, T_range=(60, 300), paged=True,
                              cache_dtype="fp8", seed=56),
@@ -73,7 +76,7 @@ def small(kind, **kw):
     return base.with_(**kw) if kw else base
 
 
-BF16_KINDS = ["contig", "tiny", "tiny_unit", "paged", "verify", "verify_h"]
+BF16_KINDS = ["contig", "tiny", "tiny_unit", "paged", "verify", "verify_h", "groups_ragged"]
 ALL_KINDS = BF16_KINDS + ["fp8", "fp8_paged"]
 
 
@@ -141,7 +144,7 @@ def test_split_count_invariance_and_determinism(mla, kind):
     np.testing.assert_array_equal(_f64(out2), results[0][1])
 
 
-@pytest.mark.parametrize("kind", ["contig", "tiny", "verify", "verify_h", "paged", "fp8"])
+@pytest.mark.parametrize("kind", ["contig", "tiny", "verify", "verify_h", "groups_ragged", "paged", "fp8"])
 @pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("part", [torch.float32, torch.bfloat16])
 def test_combine_out_equals_separate_steps(mla, kind, o_dtype, part):
