@@ -32,6 +32,12 @@ CASES = dict(
     paged=W.Workload("pf_paged", B=3, H=8, s_q=150, causal=True, T_range=(150, 420), paged=True, seed=64),
     fp8=W.Workload("pf_fp8", B=2, H=8, s_q=190, causal=True, T=190, cache_dtype="fp8", seed=65),
     tiny_q=W.Workload("pf_one", B=2, H=16, s_q=1, causal=True, T=77, seed=66),
+    # contiguous, ragged lengths with NaN padding rows up to a row stride that
+    # lies between the longest sequence and T_pad: the expansion products
+    # carry the padding into the workspace and never write its last rows;
+    # the attention must not see either
+    ragged_pad=W.Workload("pf_ragged_pad", B=3, H=8, s_q=150, causal=True, T_range=(150, 420), T_stride=448,
+                          seed=67),
 )
 
 
