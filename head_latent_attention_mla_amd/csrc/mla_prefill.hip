@@ -510,23 +510,33 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
   if (e != hipSuccess) return e;
+  bool expanded = false;
   if (!p.fp8 && p.block_table == nullptr) {
     // contiguous bf16 rows: per sequence two plain products over all heads at
     // once, in column-major terms K^T (H*128 x n) = W (H*128 x 512) C^T
     // (512 x n), with W = W_UK or W_UV^T as [H*128, 512] row-major and C the
     // rows' latent parts (row pitch 576); K^T lands token-major with leading
     // dimension kv_ld.  n = the rows the cache holds per sequence, up to T_pad.
+    // If the library has no algorithm for the shape (or no handle), the
+    // hand-written expansion below produces the same layout.
     const int64_t n = min((int64_t)p.T_pad, p.T_stride);
     const int64_t hd = (int64_t)p.H * D_NOPE;
-    for (int b = 0; b < p.B; ++b) {
+    expanded = true;
+    for (int b = 0; b < p.B && expanded; ++b) {
       const uint16_t* c = (const uint16_t*)p.rows + (int64_t)b * p.T_stride * ROWW;
       const int64_t o = (int64_t)b * p.T_pad * p.kv_ld;
-      e = gemm_bf16(true, false, hd, n, D_C, p.w_uk, D_C, c, ROWW, p.k_nope + o, p.kv_ld, 1, 0, 0, 0, stream);
-      if (e != hipSuccess) return e;
-      e = gemm_bf16(true, false, hd, n, D_C, p.w_uvt, D_C, c, ROWW, p.v + o, p.kv_ld, 1, 0, 0, 0, stream);
-      if (e != hipSuccess) return e;
+      for (int part = 0; part < 2; ++part) {
+        e = gemm_bf16(true, false, hd, n, D_C, part ? p.w_uvt : p.w_uk, D_C, c, ROWW, (part ? p.v : p.k_nope) + o,
+                      p.kv_ld, 1, 0, 0, 0, stream);
+        if (e == hipErrorNotSupported || e == hipErrorNotInitialized) {
+          expanded = false;
+          break;
+        }
+        if (e != hipSuccess) return e;
+      }
     }
-  } else {
+  }
+  if (!expanded) {
     if (p.fp8)
       hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
     else
