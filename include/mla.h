@@ -363,7 +363,12 @@ mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_
  *   workspace  ws_bytes >= mla_prefill_workspace_bytes(B, s_q, H, max_seqlen):
  *            W_UV^T, K_nope and V [B, T_pad, H * 128 + 64] (token-major) and the rope keys
  *            [B, T_pad, 64], T_pad = max_seqlen rounded up to 128.
- * s_q <= max_seqlen; 0 from mla_prefill_workspace_bytes means an invalid size. */
+ * s_q <= max_seqlen; 0 from mla_prefill_workspace_bytes means an invalid size.
+ * For contiguous bf16 caches the expansion runs as hipBLASLt matrix products:
+ * the first call on a device creates a hipBLASLt handle (allocated by that
+ * library and kept until the process ends); the products themselves use no
+ * workspace.  If the library offers no algorithm, a hand-written kernel does
+ * the expansion instead. */
 size_t mla_prefill_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
 mla_status mla_prefill_expand(const void* q, const mla_kv_desc* kv, const void* w_uk,
                               const void* w_uv, int32_t B, int32_t s_q, int32_t H,
