@@ -245,10 +245,11 @@ def latent_attention(inp: dict, q_lat: np.ndarray, scale: float,
         for j in range(s_q):
             n = visible_rows(T, s_q, j, causal)
             S = (q_lat[b, j, heads] @ C[:n].T) * scale     # [len(heads), n]
+            P = np.empty_like(S)
             for i, h in enumerate(heads):
-                p, l = _softmax_weights(S[i])
-                o[b, j, h] = p @ C[:n, :D_C]
-                lse[b, j, h] = l
+                P[i], lse[b, j, h] = _softmax_weights(S[i])
+            # every head's weighted sum of the same latent rows: one product
+            o[b, j, heads] = P @ C[:n, :D_C]
     return o, lse
 
 

@@ -1,11 +1,14 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
-Bars (floating point, bf16 inputs, fp32 accumulation): max-abs <= 2e-2 and
-relative L2 <= 5e-3 against the oracle; FP8 caches: max-abs <= 6e-2.
+Bars (floating point, bf16 inputs, fp32 accumulation): every element within
+max-abs 2e-2 of the oracle, plus -- for outputs stored as bf16 -- that
+element's own rounding to bf16, |bf16(ref) - ref|; relative L2 <= 5e-3 over
+the tensor with no allowance.  FP8 caches: max-abs 6e-2 on the same terms.
 Small cases span several 64-row tiles, a ragged tail, partial row groups and
-every cache kind; the full-size workloads are checked on sampled (b, h) pairs
-computed one by one by the naive oracle.
+every cache kind; the full-size workloads are checked over the whole output
+tensor, in the launch configuration the benchmark times.
 """
+import functools
 import math
 
 import numpy as np
@@ -41,18 +44,28 @@ def _f64(t):
     return t.detach().double().cpu().numpy()
 
 
+def bf16_rounding(ref):
+    """|bf16(ref) - ref| element by element: the part of an output's error
+    that its final rounding to bf16 accounts for (at most 2^-9 |ref|)."""
+    r = np.asarray(ref, np.float64)
+    return np.abs(O.bf16_to_f64(W.to_bf16_bits(r)) - r)
+
+
 def _assert_close(got, ref, fp8=False, what="", out_bf16=True):
-    """max-abs bar after allowing half a unit of the final bf16 rounding of the
-    output (2^-8 |ref|, which alone passes 2e-2 once |ref| >= 8), and the
-    relative-L2 bar as stated."""
+    """Every finite reference element: |got - ref| <= bar + |bf16(ref) - ref|
+    (the second term only for bf16 outputs); relative L2 over the tensor as
+    stated, without allowance.  Returns the metrics with the raw max-abs."""
     m = oracle.compare(got, ref)
     assert m["nonfinite"] == 0, (what, m)
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     fin = np.isfinite(ref)
-    allow = 2.0 ** -8 * np.abs(ref[fin]) if out_bf16 else 0.0
-    excess = float(np.max(np.abs(got[fin] - ref[fin]) - allow)) if fin.any() else 0.0
-    m["max_abs_beyond_output_rounding"] = excess
-    assert excess <= (MAX_ABS_FP8 if fp8 else MAX_ABS), (what, m)
+    err = np.abs(got[fin] - ref[fin])
+    allow = bf16_rounding(ref[fin]) if out_bf16 else np.zeros_like(err)
+    bar = MAX_ABS_FP8 if fp8 else MAX_ABS
+    m["max_abs_beyond_rounding"] = float(np.max(err - allow)) if err.size else 0.0
+    m["elements"] = int(err.size)
+    bad = int(np.count_nonzero(err > bar + allow))
+    assert bad == 0, (what, f"{bad} elements beyond the bar", m)
     if not fp8:
         assert m["rel_l2"] <= REL_L2, (what, m)
     return m
@@ -227,26 +240,73 @@ def test_large_score_range_rescale(mla):
 
 
 # ----------------------------------------------------------------------------
-# full-size workloads, sampled outputs
+# full-size workloads, whole output tensors
 # ----------------------------------------------------------------------------
+@functools.lru_cache(maxsize=1)
+def full_inputs(name):
+    """Seeded inputs of a full-size workload (the FP8 one takes a while to
+    draw, so the last one is kept for the next test that needs it)."""
+    return W.generate(W.WORKLOADS[name])
+
+
+def run_timed_configuration(mla, inp):
+    """The launch configuration the benchmark times: absorb_q, the split-T
+    scan with bf16 partials, then the fused merge + W_UV projection (asked to
+    also write the fp32 latent output and the log-sum-exps)."""
+    w = inp["workload"]
+    q, w_uk, w_uv, cache = W.to_torch(inp)
+    B, s_q, H = w.B, w.s_q, w.H
+    N = B * s_q
+    q_lat = mla.absorb_q(q.view(N, H, -1), w_uk).view(B, s_q, H, -1)
+    ws = mla.decode_partial(q_lat, cache, SCALE, w.causal, part_dtype=torch.bfloat16)
+    o_lat = torch.empty((B, s_q, H, 512), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q.device)
+    out = mla.decode_combine_out(ws, w_uv, B, s_q, H, cache.max_seqlen, o_lat=o_lat, lse=lse,
+                                 part_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    return q_lat, o_lat, lse, out.view(B, s_q, H, 128)
+
+
 @pytest.mark.parametrize("name", ["tiny", "dsv3", "mtp_verify", "ragged_paged", "fp8_cache"])
-def test_full_size_sampled(mla, name):
+def test_full_size(mla, name):
+    """Every (sequence, query token, head) of the full-size workload: the
+    latent queries against the oracle's absorption, the latent output and
+    log-sum-exp against single-latent attention on the GPU's own latent
+    queries, the projected output against the oracle's projection of the
+    GPU's own latent output; and the whole path against the naive
+    definition on sampled (sequence, head) pairs."""
     w = W.WORKLOADS[name]
     print(f"[parity-full] {name}", flush=True)
-    inp = W.generate(w)
-    q, w_uk, w_uv, cache = W.to_torch(inp)
-    out = mla.decode(q, cache, w_uk, w_uv, SCALE, w.causal)
-    torch.cuda.synchronize()
-    got = _f64(out)
+    inp = full_inputs(name)
+    fp8 = w.cache_dtype == "fp8"
+    B, s_q, H = w.B, w.s_q, w.H
+    q_lat, o_lat, lse, out = run_timed_configuration(mla, inp)
+
+    q64 = O.bf16_to_f64(inp["q"]).reshape(B * s_q, H, 192)
+    ql_ref = O.absorb_q(q64, O.bf16_to_f64(inp["w_uk"])).reshape(B, s_q, H, 576)
+    ql_got = _f64(q_lat)
+    m = _assert_close(ql_got, ql_ref, what=f"{name} absorb_q")
+    print(f"[parity-full] {name} q_lat: {m}", flush=True)
+
+    o_ref, lse_ref = O.latent_attention(inp, ql_got, SCALE)
+    m = _assert_close(_f64(o_lat), o_ref, fp8=fp8, what=f"{name} o_lat", out_bf16=False)
+    print(f"[parity-full] {name} o_lat: {m}", flush=True)
+    np.testing.assert_allclose(_f64(lse), lse_ref, rtol=0, atol=2e-3 if not fp8 else 5e-3)
+
+    out_ref = O.absorb_out(_f64(o_lat).reshape(B * s_q, H, 512), O.bf16_to_f64(inp["w_uv"]))
+    m = _assert_close(_f64(out).reshape(B * s_q, H, 128), out_ref, what=f"{name} out")
+    print(f"[parity-full] {name} out: {m}", flush=True)
+
     rng = np.random.default_rng(123)
-    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(6)]
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)]
     pairs += [(0, 0), (w.B - 1, w.H - 1)]
     ref = O.naive_decode(inp, SCALE, pairs=pairs)
+    got = _f64(out)
     sel = np.zeros(got.shape, bool)
     for b, h in pairs:
         sel[b, :, h] = True
-    m = _assert_close(got[sel], ref[sel], fp8=w.cache_dtype == "fp8", what=name)
-    print(f"[parity-full] {name}: {m}", flush=True)
+    m = _assert_close(got[sel], ref[sel], fp8=fp8, what=f"{name} vs naive")
+    print(f"[parity-full] {name} end to end: {m}", flush=True)
 
 
 # ----------------------------------------------------------------------------
