@@ -49,7 +49,7 @@ def build(verbose: bool = False, extra=()) -> str:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp,
-           f"-L{ROCM}/lib", "-lhipblaslt", f"-Wl,-rpath,{ROCM}/lib"]
+           f"-Wl,-rpath,{ROCM}/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "mla_internal.h"
 
@@ -185,11 +186,15 @@ mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_lat, int32_t N,
                                          N, H, (hipStream_t)stream));
 }
 
-size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
-                                  int32_t num_splits) {
+size_t mla_decode_workspace_bytes_ex(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
+                                     int32_t num_splits) {
   Plan pl;
   if (!make_plan(B, s_q, H, max_seqlen, num_splits, &pl)) return 0;
   return pl.ws_bytes;
+}
+
+size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
+  return mla_decode_workspace_bytes_ex(B, s_q, H, max_seqlen, 0);
 }
 
 int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen,
@@ -312,7 +317,15 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
 mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
                            int32_t H, float softmax_scale, int32_t causal, void* o_lat,
                            int32_t o_lat_dtype, float* lse, void* workspace, size_t ws_bytes,
-                           int32_t num_splits, void* stream) {
+                           void* stream) {
+  return mla_decode_attn_ex(q_lat, kv, B, s_q, H, softmax_scale, causal, o_lat, o_lat_dtype, lse, workspace,
+                            ws_bytes, 0, stream);
+}
+
+mla_status mla_decode_attn_ex(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                              int32_t H, float softmax_scale, int32_t causal, void* o_lat,
+                              int32_t o_lat_dtype, float* lse, void* workspace, size_t ws_bytes,
+                              int32_t num_splits, void* stream) {
   // validate the outputs too before anything is enqueued
   if (o_lat == nullptr) return MLA_ERR_ARG;
   if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
@@ -572,6 +585,49 @@ mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int3
                                   int32_t num_splits, int32_t part_dtype, void* stream) {
   return decode_partial_impl(q_lat, kv, B, s_q, H, softmax_scale, causal, workspace, ws_bytes, num_splits,
                              part_dtype, (hipStream_t)stream, true);
+}
+
+mla_status mla_validate_kv_host(const mla_kv_desc* kv, const int32_t* seqlens_host,
+                                const int32_t* block_table_host, int32_t B, int32_t s_q,
+                                int64_t n_pool_blocks) {
+  if (kv == nullptr || seqlens_host == nullptr || B <= 0 || s_q <= 0) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  const bool paged = kv->block_table != nullptr;
+  if (paged && (block_table_host == nullptr || n_pool_blocks <= 0)) return MLA_ERR_ARG;
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t T = seqlens_host[b];
+    if (T < s_q || T > kv->max_seqlen) return MLA_ERR_ARG;
+    if (!paged) {
+      if (T > kv->T_stride) return MLA_ERR_ARG;
+      continue;
+    }
+    if (T > (int64_t)kv->max_blocks * kTileRows) return MLA_ERR_ARG;
+    const int32_t* row = block_table_host + (int64_t)b * kv->max_blocks;
+    for (int64_t i = 0; i < (T + kTileRows - 1) / kTileRows; ++i)
+      if (row[i] < 0 || row[i] >= n_pool_blocks) return MLA_ERR_ARG;
+  }
+  return MLA_OK;
+}
+
+mla_status mla_validate_kv(const mla_kv_desc* kv, int32_t B, int32_t s_q, int64_t n_pool_blocks,
+                           void* stream) {
+  if (kv == nullptr || B <= 0 || B > (1 << 24) || s_q <= 0) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  const bool paged = kv->block_table != nullptr;
+  if (paged && n_pool_blocks <= 0) return MLA_ERR_ARG;
+  const hipStream_t st = (hipStream_t)stream;
+  std::vector<int32_t> lens((size_t)B);
+  std::vector<int32_t> table(paged ? (size_t)B * kv->max_blocks : 0);
+  if (hipMemcpyAsync(lens.data(), kv->seqlens, lens.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
+  if (paged && hipMemcpyAsync(table.data(), kv->block_table, table.size() * sizeof(int32_t),
+                              hipMemcpyDeviceToHost, st) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MLA_ERR_HIP;
+  return mla_validate_kv_host(kv, lens.data(), paged ? table.data() : nullptr, B, s_q, n_pool_blocks);
 }
 
 }  // extern "C"

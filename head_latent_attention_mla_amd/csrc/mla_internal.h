@@ -131,12 +131,6 @@ struct PrefillParams {
   int32_t fp8;
 };
 
-// Column-major C (M x N, ldc) = op(A) (M x K) op(B) (K x N) in bf16 with
-// fp32 accumulation, through hipBLASLt (mla_gemm.cpp); batch products with
-// the given element strides between consecutive A, B and C (0: shared).
-hipError_t gemm_bf16(bool trans_a, bool trans_b, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                     const void* B, int64_t ldb, void* C, int64_t ldc, int batch, int64_t stride_a,
-                     int64_t stride_b, int64_t stride_c, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);

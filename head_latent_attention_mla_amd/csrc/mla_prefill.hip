@@ -6,16 +6,13 @@
 //
 // The expansion writes K_nope and V token-major, [B, T_pad, H * 128 + 64]
 // bf16 (head h at h * 128 of a row; the pad keeps one head's rows from being
-// a power of two apart):
-//   contiguous bf16 caches: per sequence two plain matrix products over all
-//       heads at once (hipBLASLt), K = C W_UK^T and V = C W_UV;
-//   FP8 or paged caches: expand_kv_kernel, one persistent work-group per
-//       (head, K or V) that holds that half of the head's weights in LDS and
-//       streams every cached row (dequantised, gathered) through MFMA, rows
-//       past a sequence's end written as 0.
+// a power of two apart): expand_kv_kernel, one persistent work-group per
+// (head, K or V) that holds that half of the head's weights in LDS and
+// streams every cached row (contiguous or paged, bf16 or dequantised E4M3)
+// through MFMA, rows past a sequence's end written as 0.
 //   copy_rope_kernel copies the rows' rope keys to [B, T_pad, 64].
-// Rows past a sequence's end are masked in the attention (they may hold
-// anything on the first route).  Then one attention kernel:
+// Rows past a sequence's end are masked in the attention.  Then one
+// attention kernel:
 //   prefill_attn_kernel  per (128 query rows, head, sequence): causal flash
 //       attention.  Each wave owns 32 query rows: S^T = K Q^T (the K tile from
 //       LDS, the query rows held in registers), an online softmax per row,
@@ -510,40 +507,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
   hipError_t e = launch_transpose_wuv(p.w_uv, p.w_uvt, p.H, stream);
   if (e != hipSuccess) return e;
-  bool expanded = false;
-  if (!p.fp8 && p.block_table == nullptr) {
-    // contiguous bf16 rows: per sequence two plain products over all heads at
-    // once, in column-major terms K^T (H*128 x n) = W (H*128 x 512) C^T
-    // (512 x n), with W = W_UK or W_UV^T as [H*128, 512] row-major and C the
-    // rows' latent parts (row pitch 576); K^T lands token-major with leading
-    // dimension kv_ld.  n = the rows the cache holds per sequence, up to T_pad.
-    // If the library has no algorithm for the shape (or no handle), the
-    // hand-written expansion below produces the same layout.
-    const int64_t n = min((int64_t)p.T_pad, p.T_stride);
-    const int64_t hd = (int64_t)p.H * D_NOPE;
-    expanded = true;
-    for (int b = 0; b < p.B && expanded; ++b) {
-      const uint16_t* c = (const uint16_t*)p.rows + (int64_t)b * p.T_stride * ROWW;
-      const int64_t o = (int64_t)b * p.T_pad * p.kv_ld;
-      for (int part = 0; part < 2; ++part) {
-        e = gemm_bf16(true, false, hd, n, D_C, part ? p.w_uvt : p.w_uk, D_C, c, ROWW, (part ? p.v : p.k_nope) + o,
-                      p.kv_ld, 1, 0, 0, 0, stream);
-        if (e == hipErrorNotSupported || e == hipErrorNotInitialized) {
-          expanded = false;
-          break;
-        }
-        if (e != hipSuccess) return e;
-      }
-    }
-  }
-  if (!expanded) {
-    if (p.fp8)
-      hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL(expand_kv_kernel<false>, dim3(2 * p.H), dim3(256), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (p.fp8)
+    hipLaunchKernelGGL(expand_kv_kernel<true>, dim3(2 * p.H), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(expand_kv_kernel<false>, dim3(2 * p.H), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(copy_rope_kernel, dim3(p.T_pad / ET, p.B), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

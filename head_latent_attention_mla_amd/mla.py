@@ -52,10 +52,13 @@ class KVDesc(ctypes.Structure):
 _VP, _I32, _SZ, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
 SIGNATURES = {
     "mla_absorb_q": (_I32, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _VP]),
-    "mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
+    "mla_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
+    "mla_decode_workspace_bytes_ex": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "mla_decode_num_splits": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "mla_decode_attn": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _I32,
-                               _VP, _VP, _SZ, _I32, _VP]),
+                               _VP, _VP, _SZ, _VP]),
+    "mla_decode_attn_ex": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _I32,
+                                  _VP, _VP, _SZ, _I32, _VP]),
     "mla_decode_partial": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ, _I32,
                                   _I32, _VP]),
     "mla_decode_partial_fp8": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _SZ,
@@ -82,6 +85,8 @@ SIGNATURES = {
     "mla_attend_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32]),
     "mla_attend": (_I32, [_VP, ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, _I32, _F32, _I32, _VP, _VP, _SZ,
                           _VP]),
+    "mla_validate_kv": (_I32, [ctypes.POINTER(KVDesc), _I32, _I32, ctypes.c_int64, _VP]),
+    "mla_validate_kv_host": (_I32, [ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, ctypes.c_int64]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
 }
 
@@ -111,6 +116,26 @@ def _ptr(t: Optional[torch.Tensor]):
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _empty(shape, dtype, device, stream=None) -> torch.Tensor:
+    """torch.empty on ``stream`` (the current stream when None): the caching
+    allocator then hands the memory to other work only once ``stream`` has
+    passed the kernels that use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+# MLA_VALIDATE=1: check the device-resident preconditions of every cache
+# before the calls that read it (mla_validate_kv; synchronises, for debugging)
+VALIDATE = os.environ.get("MLA_VALIDATE", "0") not in ("", "0")
+
+
+def _maybe_validate(cache: "LatentCache", s_q: int, stream=None):
+    if VALIDATE:
+        cache.validate(s_q, stream)
 
 
 def _require(t: torch.Tensor, name: str, dtype, shape=None):
@@ -183,6 +208,14 @@ class LatentCache:
             d.max_blocks = 0
         return d
 
+    def validate(self, s_q: int = 1, stream=None) -> None:
+        """Check the device-resident preconditions (lengths within bounds,
+        block ids inside the pool) with mla_validate_kv; raises MLAError."""
+        kv = self.desc()
+        n_pool = int(self.rows.shape[0]) if self.paged else 0
+        _check(_lib.mla_validate_kv(ctypes.byref(kv), self.B, int(s_q), n_pool, _stream(stream)),
+               "mla_validate_kv")
+
 
 def absorb_q(q: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """q [N, H, 192] bf16, W_UK [H, 128, 512] bf16 -> latent query [N, H, 576] bf16."""
@@ -190,7 +223,7 @@ def absorb_q(q: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tensor] = 
     _require(q, "q", torch.bfloat16, (N, H, D_NOPE + D_ROPE))
     _require(w_uk, "w_uk", torch.bfloat16, (H, D_NOPE, D_C))
     if out is None:
-        out = torch.empty((N, H, ROW), dtype=torch.bfloat16, device=q.device)
+        out = _empty((N, H, ROW), torch.bfloat16, q.device, stream)
     _require(out, "q_lat", torch.bfloat16, (N, H, ROW))
     _check(_lib.mla_absorb_q(_ptr(q), _ptr(w_uk), _ptr(out), N, H, D_NOPE, D_ROPE, D_C, _stream(stream)),
            "mla_absorb_q")
@@ -198,7 +231,9 @@ def absorb_q(q: torch.Tensor, w_uk: torch.Tensor, out: Optional[torch.Tensor] = 
 
 
 def decode_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0) -> int:
-    return int(_lib.mla_decode_workspace_bytes(B, s_q, H, max_seqlen, num_splits))
+    if num_splits == 0:
+        return int(_lib.mla_decode_workspace_bytes(B, s_q, H, max_seqlen))
+    return int(_lib.mla_decode_workspace_bytes_ex(B, s_q, H, max_seqlen, num_splits))
 
 
 def decode_num_splits(B: int, s_q: int, H: int, max_seqlen: int, num_splits: int = 0) -> int:
@@ -218,18 +253,24 @@ def decode_attn(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_
     kv = cache.desc()
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
     if o_lat is None:
-        o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=q_lat.device)
+        o_lat = _empty((B, s_q, H, D_C), o_dtype, q_lat.device, stream)
     _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
     if lse is None and want_lse:
-        lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device)
+        lse = _empty((B, s_q, H), torch.float32, q_lat.device, stream)
     if lse is not None:
         _require(lse, "lse", torch.float32, (B, s_q, H))
     need = decode_workspace_bytes(B, s_q, H, cache.max_seqlen, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
-    _check(_lib.mla_decode_attn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
-                                _ptr(o_lat), dt, _ptr(lse), _ptr(workspace), workspace.numel(), num_splits,
-                                _stream(stream)), "mla_decode_attn")
+        workspace = _empty(max(need, 1), torch.uint8, q_lat.device, stream)
+    _maybe_validate(cache, s_q, stream)
+    if num_splits == 0:
+        _check(_lib.mla_decode_attn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
+                                    _ptr(o_lat), dt, _ptr(lse), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "mla_decode_attn")
+    else:
+        _check(_lib.mla_decode_attn_ex(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
+                                       _ptr(o_lat), dt, _ptr(lse), _ptr(workspace), workspace.numel(), num_splits,
+                                       _stream(stream)), "mla_decode_attn_ex")
     return o_lat, lse
 
 
@@ -249,7 +290,8 @@ def decode_partial(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAU
     kv = cache.desc()
     need = decode_workspace_bytes(B, s_q, H, cache.max_seqlen, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+        workspace = _empty(max(need, 1), torch.uint8, q_lat.device, stream)
+    _maybe_validate(cache, s_q, stream)
     fn, name = ((_lib.mla_decode_partial_fp8, "mla_decode_partial_fp8") if fp8_math
                 else (_lib.mla_decode_partial, "mla_decode_partial"))
     _check(fn(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
@@ -263,7 +305,7 @@ def decode_combine(workspace: torch.Tensor, B: int, s_q: int, H: int, max_seqlen
     """Phase 2 of decode_attn: merge the split partials held in ``workspace``."""
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
     if o_lat is None:
-        o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=workspace.device)
+        o_lat = _empty((B, s_q, H, D_C), o_dtype, workspace.device, stream)
     _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
     if lse is not None:
         _require(lse, "lse", torch.float32, (B, s_q, H))
@@ -282,7 +324,7 @@ def decode_combine_out(workspace: torch.Tensor, w_uv: torch.Tensor, B: int, s_q:
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
     _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
     if out is None:
-        out = torch.empty((B * s_q, H, D_V), dtype=torch.bfloat16, device=workspace.device)
+        out = _empty((B * s_q, H, D_V), torch.bfloat16, workspace.device, stream)
     _require(out, "out", torch.bfloat16, (B * s_q, H, D_V))
     if o_lat is not None:
         _require(o_lat, "o_lat", o_dtype, (B, s_q, H, D_C))
@@ -302,7 +344,7 @@ def absorb_out(o_lat: torch.Tensor, w_uv: torch.Tensor, out: Optional[torch.Tens
     _require(o_lat, "o_lat", o_lat.dtype, (N, H, D_C))
     _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
     if out is None:
-        out = torch.empty((N, H, D_V), dtype=torch.bfloat16, device=o_lat.device)
+        out = _empty((N, H, D_V), torch.bfloat16, o_lat.device, stream)
     _require(out, "out", torch.bfloat16, (N, H, D_V))
     _check(_lib.mla_absorb_out(_ptr(o_lat), dt, _ptr(w_uv), _ptr(out), N, H, D_C, D_V, _stream(stream)),
            "mla_absorb_out")
@@ -354,7 +396,7 @@ def sparse_decode_partial(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torc
     kv = cache.desc()
     need = sparse_workspace_bytes(B, s_q, H, k_max, num_splits, cache.fp8)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+        workspace = _empty(max(need, 1), torch.uint8, q_lat.device, stream)
     _check(_lib.mla_sparse_decode_partial(_ptr(q_lat), ctypes.byref(kv), _ptr(sel_idx), _ptr(sel_count), k_max,
                                           B, s_q, H, float(scale), _ptr(workspace), workspace.numel(), num_splits,
                                           _part_code(part_dtype), _stream(stream)), "mla_sparse_decode_partial")
@@ -368,11 +410,11 @@ def sparse_decode_attn(q_lat: torch.Tensor, cache: LatentCache, sel_idx: torch.T
     B, s_q, H, k_max = _sparse_args(q_lat, cache, sel_idx, sel_count)
     kv = cache.desc()
     dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_dtype]
-    o_lat = torch.empty((B, s_q, H, D_C), dtype=o_dtype, device=q_lat.device)
-    lse = torch.empty((B, s_q, H), dtype=torch.float32, device=q_lat.device) if want_lse else None
+    o_lat = _empty((B, s_q, H, D_C), o_dtype, q_lat.device, stream)
+    lse = _empty((B, s_q, H), torch.float32, q_lat.device, stream) if want_lse else None
     need = sparse_workspace_bytes(B, s_q, H, k_max, num_splits, cache.fp8)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_lat.device)
+        workspace = _empty(max(need, 1), torch.uint8, q_lat.device, stream)
     _check(_lib.mla_sparse_decode_attn(_ptr(q_lat), ctypes.byref(kv), _ptr(sel_idx), _ptr(sel_count), k_max,
                                        B, s_q, H, float(scale), _ptr(o_lat), dt, _ptr(lse), _ptr(workspace),
                                        workspace.numel(), num_splits, _stream(stream)), "mla_sparse_decode_attn")
@@ -406,10 +448,11 @@ def naive_decode(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: 
     _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
     kv = cache.desc()
     if out is None:
-        out = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=q.device)
+        out = _empty((B, s_q, H, D_V), torch.bfloat16, q.device, stream)
     need = naive_workspace_bytes(B, s_q, H, cache.max_seqlen)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 1), torch.uint8, q.device, stream)
+    _maybe_validate(cache, s_q, stream)
     _check(_lib.mla_naive_decode(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
                                  int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "mla_naive_decode")
@@ -435,7 +478,7 @@ def latent_append(x: torch.Tensor, w_dkr: torch.Tensor, seq_id: torch.Tensor, po
     kv = cache.desc()
     need = append_workspace_bytes(N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _empty(max(need, 1), torch.uint8, x.device, stream)
     _check(_lib.mla_latent_append(_ptr(x), _ptr(w_dkr), N, d, _ptr(seq_id), _ptr(pos), float(rope_base),
                                   ctypes.byref(kv), cache.B, _ptr(workspace), workspace.numel(),
                                   _stream(stream)), "mla_latent_append")
@@ -445,14 +488,14 @@ def prefill_workspace_bytes(B: int, s_q: int, H: int, max_seqlen: int) -> int:
     return int(_lib.mla_prefill_workspace_bytes(B, s_q, H, max_seqlen))
 
 
-def _attend_args(q, cache, w_uk, w_uv, out):
+def _attend_args(q, cache, w_uk, w_uv, out, stream=None):
     B, s_q, H = q.shape[0], q.shape[1], q.shape[2]
     _require(q, "q", torch.bfloat16, (B, s_q, H, D_NOPE + D_ROPE))
     _require(w_uk, "w_uk", torch.bfloat16, (H, D_NOPE, D_C))
     _require(w_uv, "w_uv", torch.bfloat16, (H, D_C, D_V))
     kv = cache.desc()
     if out is None:
-        out = torch.empty((B, s_q, H, D_V), dtype=torch.bfloat16, device=q.device)
+        out = _empty((B, s_q, H, D_V), torch.bfloat16, q.device, stream)
     _require(out, "out", torch.bfloat16, (B, s_q, H, D_V))
     return B, s_q, H, kv, out
 
@@ -462,10 +505,11 @@ def prefill_expand(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv
                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Expand path: every cached row expanded per head into K and V, then
     attention with the 192-wide queries. Same I/O as decode()/naive_decode()."""
-    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out)
+    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out, stream)
     need = prefill_workspace_bytes(B, s_q, H, cache.max_seqlen)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 1), torch.uint8, q.device, stream)
+    _maybe_validate(cache, s_q, stream)
     _check(_lib.mla_prefill_expand(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
                                    int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(),
                                    _stream(stream)), "mla_prefill_expand")
@@ -488,10 +532,11 @@ def attend(q: torch.Tensor, cache: LatentCache, w_uk: torch.Tensor, w_uv: torch.
            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Absorbed or expand path, whichever costs fewer FLOPs for s_q query
     tokens against max_seqlen cached rows."""
-    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out)
+    B, s_q, H, kv, out = _attend_args(q, cache, w_uk, w_uv, out, stream)
     need = attend_workspace_bytes(B, s_q, H, cache.max_seqlen)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _empty(max(need, 1), torch.uint8, q.device, stream)
+    _maybe_validate(cache, s_q, stream)
     _check(_lib.mla_attend(_ptr(q), ctypes.byref(kv), _ptr(w_uk), _ptr(w_uv), B, s_q, H, float(scale),
                            int(bool(causal)), _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
            "mla_attend")

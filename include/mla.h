@@ -23,7 +23,8 @@
  *
  * Conventions for every call:
  *   - Every pointer is a DEVICE pointer unless marked "host".  The caller owns
- *     all memory; the library never allocates, frees or keeps device memory.
+ *     all memory: the library never allocates or frees memory and keeps no
+ *     host state between calls.
  *   - Tensors are dense and row-major with the last dimension contiguous.
  *     bf16 is the 16-bit brain float; fp8 is OCP FP8 E4M3 ("e4m3fn").
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
@@ -39,6 +40,7 @@
  *     seqlens[b] <= T_stride (contiguous) or <= max_blocks * 64 (paged), and
  *     every block id in the first ceil(seqlens[b] / 64) entries of a row of the
  *     block table is a valid pool block.  Entries past that are never read.
+ *     mla_validate_kv checks them (a debugging aid that synchronises).
  *   - Calls are reentrant; results for a fixed argument set are bitwise
  *     reproducible run to run (no floating-point atomics).
  */
@@ -108,15 +110,19 @@ mla_status mla_absorb_q(const void* q, const void* w_uk, void* q_lat,
                         int32_t N, int32_t H, int32_t d_nope, int32_t d_rope,
                         int32_t d_c, void* stream);
 
-/* Bytes of device workspace mla_decode_attn needs for these sizes.
- * num_splits: the number of parts a sequence of max_seqlen rows is scanned
- * in; 0 lets the library choose, a positive value forces it (any count gives
- * the same result up to rounding; it is capped at ceil(max_seqlen / 64)).
- * Returns 0 for invalid sizes. */
-size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H,
-                                  int32_t max_seqlen, int32_t num_splits);
+/* Bytes of device workspace mla_decode_attn needs for these sizes, with the
+ * library's own split count.  Returns 0 for invalid sizes. */
+size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
 
-/* The split count S mla_decode_attn will use for these sizes (host integers only). */
+/* The same for mla_decode_attn_ex and the split-level calls below.
+ * num_splits: the number of parts a sequence of max_seqlen rows is scanned
+ * in; 0 lets the library choose (then equal to mla_decode_workspace_bytes), a
+ * positive value forces it (any count gives the same result up to rounding;
+ * it is capped at ceil(max_seqlen / 64)).  Returns 0 for invalid sizes. */
+size_t mla_decode_workspace_bytes_ex(int32_t B, int32_t s_q, int32_t H,
+                                     int32_t max_seqlen, int32_t num_splits);
+
+/* The split count S the scan will use for these sizes (host integers only). */
 int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H,
                               int32_t max_seqlen, int32_t num_splits);
 
@@ -145,25 +151,35 @@ int32_t mla_decode_num_splits(int32_t B, int32_t s_q, int32_t H,
  * lse          fp32 [B, s_q, H], or NULL when not wanted
  * workspace    device scratch of ws_bytes >= mla_decode_workspace_bytes(...);
  *              contents on entry are ignored; it may be reused after the
- *              stream has finished the call.
- * num_splits   0 = library choice, else the forced split count. */
+ *              stream has finished the call. */
 mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv,
                            int32_t B, int32_t s_q, int32_t H,
                            float softmax_scale, int32_t causal,
                            void* o_lat, int32_t o_lat_dtype, float* lse,
-                           void* workspace, size_t ws_bytes, int32_t num_splits,
-                           void* stream);
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* mla_decode_attn with the split count forced (num_splits as for
+ * mla_decode_workspace_bytes_ex; ws_bytes >= that figure).  num_splits = 0
+ * is mla_decode_attn. */
+mla_status mla_decode_attn_ex(const void* q_lat, const mla_kv_desc* kv,
+                              int32_t B, int32_t s_q, int32_t H,
+                              float softmax_scale, int32_t causal,
+                              void* o_lat, int32_t o_lat_dtype, float* lse,
+                              void* workspace, size_t ws_bytes, int32_t num_splits,
+                              void* stream);
 
 /* Steps 2 and 3 as two separate calls, for callers that keep or move the
  * split partials themselves (for example to merge ranges of one sequence that
  * were scanned on different devices).  mla_decode_attn is exactly
  * mla_decode_partial followed by mla_decode_combine on the same workspace.
  *
- * mla_decode_partial: same arguments as mla_decode_attn minus the outputs,
+ * mla_decode_partial: same arguments as mla_decode_attn_ex minus the outputs,
  *   plus part_dtype, the element type of the partial outputs: MLA_FP32, or
  *   MLA_BF16 (each value rounded to nearest even: half the partial traffic,
  *   about 2^-9 relative error on each partial; mla_decode_attn uses the
  *   precision of its o_lat_dtype).  Any other value gives MLA_ERR_ARG.
+ *   ws_bytes >= mla_decode_workspace_bytes_ex(B, s_q, H, kv->max_seqlen,
+ *   num_splits).
  *   Scans every part and writes into the workspace, with
  *   S = mla_decode_num_splits(B, s_q, H, kv->max_seqlen, num_splits),
  *   R = s_q * H and M = B * (S + 1) partial slots (aligned = rounded up to a
@@ -364,11 +380,7 @@ mla_status mla_latent_append(const void* x, const void* w_dkr, int32_t N, int32_
  *            W_UV^T, K_nope and V [B, T_pad, H * 128 + 64] (token-major) and the rope keys
  *            [B, T_pad, 64], T_pad = max_seqlen rounded up to 128.
  * s_q <= max_seqlen; 0 from mla_prefill_workspace_bytes means an invalid size.
- * For contiguous bf16 caches the expansion runs as hipBLASLt matrix products:
- * the first call on a device creates a hipBLASLt handle (allocated by that
- * library and kept until the process ends); the products themselves use no
- * workspace.  If the library offers no algorithm, a hand-written kernel does
- * the expansion instead. */
+ * The expansion is a hand-written kernel for every cache kind. */
 size_t mla_prefill_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
 mla_status mla_prefill_expand(const void* q, const mla_kv_desc* kv, const void* w_uk,
                               const void* w_uv, int32_t B, int32_t s_q, int32_t H,
@@ -389,6 +401,26 @@ size_t mla_attend_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max
 mla_status mla_attend(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
                       int32_t B, int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
                       void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Check of the device-resident preconditions of a cache description (a
+ * debugging aid: the lengths and the block table are copied to the host and
+ * the call waits for the copies on `stream`).  For every b < B:
+ *   s_q <= seqlens[b] <= kv->max_seqlen;
+ *   contiguous: seqlens[b] <= kv->T_stride;
+ *   paged: seqlens[b] <= kv->max_blocks * 64, and every block id in the first
+ *   ceil(seqlens[b] / 64) entries of row b of the block table lies in
+ *   [0, n_pool_blocks).
+ * n_pool_blocks: blocks in the pool (paged caches; ignored otherwise).
+ * Returns MLA_OK, MLA_ERR_ARG (a precondition or an argument fails),
+ * MLA_ERR_UNSUPPORTED (block size other than 64) or MLA_ERR_HIP (a copy
+ * failed).  mla_validate_kv_host does the same on host copies of the arrays
+ * (seqlens_host [B]; block_table_host [B, max_blocks], NULL for a
+ * contiguous cache) and makes no HIP call. */
+mla_status mla_validate_kv(const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                           int64_t n_pool_blocks, void* stream);
+mla_status mla_validate_kv_host(const mla_kv_desc* kv, const int32_t* seqlens_host,
+                                const int32_t* block_table_host, int32_t B, int32_t s_q,
+                                int64_t n_pool_blocks);
 
 /* Static, human-readable name of a status code (host). */
 const char* mla_status_string(mla_status s);

@@ -51,9 +51,23 @@ def test_status_strings(m):
         assert m._lib.mla_status_string(s).decode().startswith("MLA_")
 
 
+def test_decode_signatures_follow_the_boundary_statement():
+    """mla_decode_workspace_bytes and mla_decode_attn take exactly the
+    arguments of the boundary statement (no split control: that is the _ex
+    calls' extra argument)."""
+    text = open(HEADER).read()
+    flat = " ".join(text.split())
+    assert "size_t mla_decode_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);" in flat
+    assert ("mla_status mla_decode_attn(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q, "
+            "int32_t H, float softmax_scale, int32_t causal, void* o_lat, int32_t o_lat_dtype, float* lse, "
+            "void* workspace, size_t ws_bytes, void* stream);") in flat
+
+
 def test_workspace_and_split_plan(m):
-    ws = m._lib.mla_decode_workspace_bytes
+    ws = m._lib.mla_decode_workspace_bytes_ex
     ns = m._lib.mla_decode_num_splits
+    for B, s_q, H, T in ((64, 1, 128, 4096), (32, 4, 128, 8192), (2, 1, 16, 256), (5, 3, 40, 999)):
+        assert m._lib.mla_decode_workspace_bytes(B, s_q, H, T) == ws(B, s_q, H, T, 0)
     # DeepSeek-V3 shape: 64 sequences x 1 row group -> 4 parts of 1024 rows each;
     # B * (S + 1) = 320 partial slots of 128 rows, then the two [B] int32 tables
     assert ns(64, 1, 128, 4096, 0) == 4
@@ -78,8 +92,11 @@ def _kv(**kw):
 
 
 def _attn(m, kv, B=2, s_q=1, H=16, scale=0.07, causal=0, o_dtype=2, ws_bytes=1 << 30, ns=0, ql=0x3000, o=0x4000):
-    return m._lib.mla_decode_attn(ql, ctypes.byref(kv), B, s_q, H, scale, causal, o, o_dtype, None,
-                                  0x5000, ws_bytes, ns, None)
+    if ns == 0:
+        return m._lib.mla_decode_attn(ql, ctypes.byref(kv), B, s_q, H, scale, causal, o, o_dtype, None,
+                                      0x5000, ws_bytes, None)
+    return m._lib.mla_decode_attn_ex(ql, ctypes.byref(kv), B, s_q, H, scale, causal, o, o_dtype, None,
+                                     0x5000, ws_bytes, ns, None)
 
 
 def test_decode_attn_rejects_bad_arguments(m):
@@ -147,7 +164,7 @@ def test_naive_rejects_bad_arguments(m):
 
 def test_combine_out_rejects_bad_arguments(m):
     co = m._lib.mla_decode_combine_out
-    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256)
     assert co(2, 1, 16, 256, 0, 2, 0x1000, need, None, 0x2000, None, 2, None, None) == ARG     # no w_uv
     assert co(2, 1, 16, 256, 0, 2, 0x1000, need, 0x3000, None, None, 2, None, None) == ARG     # no out
     assert co(2, 1, 16, 256, 0, 2, 0x1000, need, 0x3000, 0x2000, None, 1, None, None) == ARG   # fp8 o_lat
@@ -159,7 +176,7 @@ def test_combine_out_rejects_bad_arguments(m):
 
 def test_sparse_rejects_bad_arguments(m):
     wsb = m._lib.mla_sparse_workspace_bytes
-    base = m._lib.mla_decode_workspace_bytes(2, 1, 16, 64, 0)
+    base = m._lib.mla_decode_workspace_bytes(2, 1, 16, 64)
     assert wsb(2, 1, 16, 64, 0, 0) == base + 2 * 64 * 576 * 2 + 256             # + compact bf16 rows + counts
     assert wsb(2, 1, 16, 64, 0, 1) == base + 2 * 64 * 576 + 256 + 512           # + e4m3 rows + counts + scales
     assert wsb(2, 1, 16, 0, 0, 0) == 0 and wsb(2, 1, 16, 64, 0, 2) == 0
@@ -223,7 +240,7 @@ def test_prefill_dispatch_and_workspace(m):
     aw = m._lib.mla_attend_workspace_bytes
     assert aw(2, 300, 16, 300) == pw(2, 300, 16, 300)                      # expand path
     q_lat = 2 * 4 * 16 * 576 * 2
-    assert aw(2, 4, 16, 300) == q_lat + m._lib.mla_decode_workspace_bytes(2, 4, 16, 300, 0)   # absorbed path
+    assert aw(2, 4, 16, 300) == q_lat + m._lib.mla_decode_workspace_bytes(2, 4, 16, 300)   # absorbed path
     pe = m._lib.mla_prefill_expand
     need = pw(2, 4, 16, 256)
     args = [0x1000, ctypes.byref(_kv()), 0x2000, 0x3000, 2, 4, 16, 0.07, 1, 0x4000, 0x5000, need, None]
@@ -243,7 +260,7 @@ def test_prefill_dispatch_and_workspace(m):
 
 def test_fp8_math_requires_an_fp8_cache(m):
     f = m._lib.mla_decode_partial_fp8
-    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256)
     assert f(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, 2, None) == UNSUP   # bf16 cache
     assert f(None, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need, 0, 2, None) == ARG
     assert f(0x3000, ctypes.byref(_kv(dtype=1, row_scale=0x6000)), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0, 2,
@@ -253,7 +270,7 @@ def test_fp8_math_requires_an_fp8_cache(m):
 def test_partial_dtype_is_checked(m):
     """Partials are fp32 (MLA_FP32 = 2) or bf16 (MLA_BF16 = 0); anything else
     is rejected before any launch, by the scans and by both merges."""
-    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256, 0)
+    need = m._lib.mla_decode_workspace_bytes(2, 1, 16, 256)
     dp = m._lib.mla_decode_partial
     for bad in (1, 3, -1):
         assert dp(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need, 0, bad, None) == ARG
@@ -262,3 +279,40 @@ def test_partial_dtype_is_checked(m):
         assert m._lib.mla_decode_combine(2, 1, 16, 256, 0, bad, 0x5000, need, 0x2000, 2, None, None) == ARG
     assert dp(0x3000, ctypes.byref(_kv()), 2, 1, 16, 0.07, 0, 0x5000, need - 1, 0, 0, None) == WS
     assert m._lib.mla_decode_combine(2, 1, 16, 256, 0, 0, 0x5000, need - 1, 0x2000, 2, None, None) == WS
+
+
+def _host_i32(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def test_validator_on_host_arrays(m):
+    """mla_validate_kv_host: every device-resident precondition of the cache
+    description, checked on host copies of the lengths and the block table."""
+    v = m._lib.mla_validate_kv_host
+    kv = _kv(T_stride=300, max_seqlen=256)
+    keep, lens = _host_i32([256, 3])
+    assert v(ctypes.byref(kv), lens, None, 2, 1, 0) == OK
+    assert v(ctypes.byref(kv), lens, None, 2, 3, 0) == OK            # s_q = 3 <= every length
+    assert v(ctypes.byref(kv), lens, None, 2, 4, 0) == ARG           # s_q = 4 > seqlens[1]
+    keep, lens = _host_i32([257, 3])
+    assert v(ctypes.byref(kv), lens, None, 2, 1, 0) == ARG           # above max_seqlen
+    kv2 = _kv(T_stride=200, max_seqlen=200)
+    keep, lens = _host_i32([200, 0])
+    assert v(ctypes.byref(kv2), lens, None, 2, 1, 0) == ARG          # a length below s_q
+    assert v(ctypes.byref(kv2), lens, None, 0, 1, 0) == ARG          # B = 0
+    assert v(ctypes.byref(kv2), None, None, 2, 1, 0) == ARG          # no lengths
+    # paged: 3 blocks per row, pool of 10 blocks; entries past ceil(T / 64) are never read
+    kvp = _kv(block_table=0x7000, block_size=64, max_blocks=3, max_seqlen=192)
+    keep, lens = _host_i32([130, 64])
+    keep2, table = _host_i32([0, 9, 4, 5, -1, 77])
+    assert v(ctypes.byref(kvp), lens, table, 2, 1, 10) == OK
+    assert v(ctypes.byref(kvp), lens, table, 2, 1, 9) == ARG         # block id 9 outside a pool of 9
+    assert v(ctypes.byref(kvp), lens, None, 2, 1, 10) == ARG         # paged without its table
+    keep2, table = _host_i32([0, 9, -4, 5, -1, 77])
+    assert v(ctypes.byref(kvp), lens, table, 2, 1, 10) == ARG        # a negative id in use
+    keep, lens = _host_i32([130, 65])
+    keep2, table = _host_i32([0, 9, 4, 5, -1, 77])
+    assert v(ctypes.byref(kvp), lens, table, 2, 1, 10) == ARG        # row 1 needs its second block (-1)
+    kvb = _kv(block_table=0x7000, block_size=32, max_blocks=3, max_seqlen=96)
+    assert v(ctypes.byref(kvb), lens, table, 2, 1, 10) == UNSUP
