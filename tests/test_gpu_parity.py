@@ -51,16 +51,56 @@ def bf16_rounding(ref):
     return np.abs(O.bf16_to_f64(W.to_bf16_bits(r)) - r)
 
 
-def _assert_close(got, ref, fp8=False, what="", out_bf16=True):
+def materialisation_bound(inp, scale, causal=None, u=2.0 ** -9, pairs=None):
+    """First-order bound, per output element, of the effect of storing every
+    expanded key and value element in bf16 (relative rounding <= u), as the
+    expand path and the naive ablation do (their keys and values are
+    materialised in bf16 before the attention).  With p = softmax(s),
+    s_t = scale <q, k_t> and out = sum_t p_t V_t:
+      values:  |sum_t p_t V_t eps_t|              <= u sum_t p_t |V_t|
+      keys:    |sum_t p_t ds_t (V_t - out)|       <= u sum_t p_t a_t |V_t - out|,
+               a_t = scale sum_k |q_k K_nope[t, k]| (the rope keys are copied).
+    Computed from the fp64 expansion of the oracle's inputs, for the listed
+    (b, h) pairs only when ``pairs`` is given (zero elsewhere)."""
+    w = inp["workload"]
+    causal = w.causal if causal is None else causal
+    q = O.bf16_to_f64(inp["q"])
+    w_uk, w_uv = O.bf16_to_f64(inp["w_uk"]), O.bf16_to_f64(inp["w_uv"])
+    B, s_q, H, _ = q.shape
+    bound = np.zeros((B, s_q, H, 128))
+    pairs = [(b, h) for b in range(B) for h in range(H)] if pairs is None else list(pairs)
+    for b in sorted({pb for pb, _ in pairs}):
+        T = int(inp["seqlens"][b])
+        C = O.sequence_rows(inp, b)
+        lat, rope = C[:, :512], C[:, 512:]
+        for h in sorted({ph for pb, ph in pairs if pb == b}):
+            K = lat @ w_uk[h].T
+            V = lat @ w_uv[h]
+            for j in range(s_q):
+                n = O.visible_rows(T, s_q, j, causal)
+                s = (K[:n] @ q[b, j, h, :128] + rope[:n] @ q[b, j, h, 128:]) * scale
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                out = p @ V[:n]
+                a = scale * (np.abs(K[:n]) @ np.abs(q[b, j, h, :128]))
+                bound[b, j, h] = u * (p @ np.abs(V[:n]) + (p * a) @ np.abs(V[:n] - out))
+    return bound
+
+
+def _assert_close(got, ref, fp8=False, what="", out_bf16=True, extra_allow=None):
     """Every finite reference element: |got - ref| <= bar + |bf16(ref) - ref|
-    (the second term only for bf16 outputs); relative L2 over the tensor as
-    stated, without allowance.  Returns the metrics with the raw max-abs."""
+    (the second term only for bf16 outputs) + extra_allow (the bound of a
+    path's stated intermediate rounding, where it has one); relative L2 over
+    the tensor as stated, without allowance.  Returns the metrics with the
+    raw max-abs."""
     m = oracle.compare(got, ref)
     assert m["nonfinite"] == 0, (what, m)
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     fin = np.isfinite(ref)
     err = np.abs(got[fin] - ref[fin])
     allow = bf16_rounding(ref[fin]) if out_bf16 else np.zeros_like(err)
+    if extra_allow is not None:
+        allow = allow + np.broadcast_to(extra_allow, ref.shape)[fin]
     bar = MAX_ABS_FP8 if fp8 else MAX_ABS
     m["max_abs_beyond_rounding"] = float(np.max(err - allow)) if err.size else 0.0
     m["elements"] = int(err.size)
