@@ -337,6 +337,28 @@ mla_status mla_decode_attn_ex(const void* q_lat, const mla_kv_desc* kv, int32_t 
                              o_lat_dtype, lse, (hipStream_t)stream);
 }
 
+size_t mla_decode_noalloc_max_bytes(void) { return mla::NOALLOC_SCRATCH_BYTES; }
+
+mla_status mla_decode_attn_noalloc(const void* q_lat, const mla_kv_desc* kv, int32_t B, int32_t s_q,
+                                   int32_t H, float softmax_scale, int32_t causal, void* o_lat,
+                                   int32_t o_lat_dtype, float* lse, void* stream) {
+  // every argument check of mla_decode_attn, before any HIP call
+  if (q_lat == nullptr || o_lat == nullptr) return MLA_ERR_ARG;
+  if (o_lat_dtype != MLA_FP32 && o_lat_dtype != MLA_BF16) return MLA_ERR_ARG;
+  if (B <= 0 || s_q <= 0 || H <= 0) return MLA_ERR_ARG;
+  if (causal != 0 && causal != 1) return MLA_ERR_ARG;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.f)) return MLA_ERR_ARG;
+  const mla_status ks = check_kv(kv, s_q);
+  if (ks != MLA_OK) return ks;
+  Plan pl;
+  if (!make_plan(B, s_q, H, kv->max_seqlen, 0, &pl)) return MLA_ERR_ARG;
+  if (pl.ws_bytes > mla::NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (mla::noalloc_scratch(&scratch) != hipSuccess) return MLA_ERR_HIP;
+  return mla_decode_attn(q_lat, kv, B, s_q, H, softmax_scale, causal, o_lat, o_lat_dtype, lse, scratch,
+                         mla::NOALLOC_SCRATCH_BYTES, stream);
+}
+
 mla_status mla_absorb_out(const void* o_lat, int32_t o_lat_dtype, const void* w_uv, void* out,
                           int32_t N, int32_t H, int32_t d_c, int32_t d_v, void* stream) {
   if (o_lat == nullptr || w_uv == nullptr || out == nullptr) return MLA_ERR_ARG;

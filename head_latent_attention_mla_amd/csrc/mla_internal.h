@@ -131,6 +131,12 @@ struct PrefillParams {
   int32_t fp8;
 };
 
+// Allocation-free decode: the split workspace is a file-scope device array of
+// this many bytes (mla_noalloc.hip); noalloc_scratch() gives the current
+// device's address of it (looked up once per device).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);

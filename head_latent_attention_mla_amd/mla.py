@@ -87,6 +87,9 @@ SIGNATURES = {
                           _VP]),
     "mla_validate_kv": (_I32, [ctypes.POINTER(KVDesc), _I32, _I32, ctypes.c_int64, _VP]),
     "mla_validate_kv_host": (_I32, [ctypes.POINTER(KVDesc), _VP, _VP, _I32, _I32, ctypes.c_int64]),
+    "mla_decode_noalloc_max_bytes": (_SZ, []),
+    "mla_decode_attn_noalloc": (_I32, [_VP, ctypes.POINTER(KVDesc), _I32, _I32, _I32, _F32, _I32, _VP, _I32,
+                                       _VP, _VP]),
     "mla_status_string": (ctypes.c_char_p, [_I32]),
 }
 
@@ -271,6 +274,28 @@ def decode_attn(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_
         _check(_lib.mla_decode_attn_ex(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale), int(bool(causal)),
                                        _ptr(o_lat), dt, _ptr(lse), _ptr(workspace), workspace.numel(), num_splits,
                                        _stream(stream)), "mla_decode_attn_ex")
+    return o_lat, lse
+
+
+def decode_attn_noalloc(q_lat: torch.Tensor, cache: LatentCache, scale: float = DEFAULT_SCALE,
+                        causal: bool = False, o_lat: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, stream=None):
+    """decode_attn with the split workspace inside the library (no
+    allocation by the library; the outputs must be given).  Calls that
+    overlap on one GPU race on that workspace."""
+    B, s_q, H = q_lat.shape[0], q_lat.shape[1], q_lat.shape[2]
+    _require(q_lat, "q_lat", torch.bfloat16, (B, s_q, H, ROW))
+    if o_lat is None:
+        raise ValueError("decode_attn_noalloc needs its output tensor")
+    dt = {torch.float32: MLA_FP32, torch.bfloat16: MLA_BF16}[o_lat.dtype]
+    _require(o_lat, "o_lat", o_lat.dtype, (B, s_q, H, D_C))
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, s_q, H))
+    kv = cache.desc()
+    _maybe_validate(cache, s_q, stream)
+    _check(_lib.mla_decode_attn_noalloc(_ptr(q_lat), ctypes.byref(kv), B, s_q, H, float(scale),
+                                        int(bool(causal)), _ptr(o_lat), dt, _ptr(lse), _stream(stream)),
+           "mla_decode_attn_noalloc")
     return o_lat, lse
 
 

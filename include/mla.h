@@ -168,6 +168,29 @@ mla_status mla_decode_attn_ex(const void* q_lat, const mla_kv_desc* kv,
                               void* workspace, size_t ws_bytes, int32_t num_splits,
                               void* stream);
 
+/* Steps 2 and 3 without any allocation: mla_decode_attn with its workspace
+ * in a fixed device array inside the library instead of a caller buffer.
+ * For callers that cannot allocate memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).
+ *   Arguments and results as mla_decode_attn (library split count).
+ *   The array holds mla_decode_noalloc_max_bytes() = 64 MiB; argument sets
+ *   whose mla_decode_workspace_bytes(...) exceeds it get MLA_ERR_WORKSPACE
+ *   before anything is enqueued (for example B = 64, H = 128, 4096 rows with
+ *   an fp32 o_lat needs 84 MB; with a bf16 o_lat, 42 MB).
+ *   Each GPU the library runs on holds its own copy of the array until the
+ *   process ends; its address is looked up once per device on the first call
+ *   there (no allocation: hipGetSymbolAddress).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, other threads) race and must be serialised by the
+ *   caller.  The kernels write every scratch byte before they read it, so
+ *   what an earlier call left there does not matter. */
+size_t mla_decode_noalloc_max_bytes(void);
+mla_status mla_decode_attn_noalloc(const void* q_lat, const mla_kv_desc* kv,
+                                   int32_t B, int32_t s_q, int32_t H,
+                                   float softmax_scale, int32_t causal,
+                                   void* o_lat, int32_t o_lat_dtype, float* lse,
+                                   void* stream);
+
 /* Steps 2 and 3 as two separate calls, for callers that keep or move the
  * split partials themselves (for example to merge ranges of one sequence that
  * were scanned on different devices).  mla_decode_attn is exactly

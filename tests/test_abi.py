@@ -316,3 +316,24 @@ def test_validator_on_host_arrays(m):
     assert v(ctypes.byref(kvp), lens, table, 2, 1, 10) == ARG        # row 1 needs its second block (-1)
     kvb = _kv(block_table=0x7000, block_size=32, max_blocks=3, max_seqlen=96)
     assert v(ctypes.byref(kvb), lens, table, 2, 1, 10) == UNSUP
+
+
+def test_noalloc_checks_before_any_hip_call(m):
+    """mla_decode_attn_noalloc rejects bad arguments and argument sets whose
+    workspace exceeds its scratch array without a HIP call."""
+    na = m._lib.mla_decode_attn_noalloc
+    cap = m._lib.mla_decode_noalloc_max_bytes()
+    assert cap == 64 << 20
+
+    def call(kv, B=2, s_q=1, H=16, o_dtype=2, ql=0x3000, o=0x4000, scale=0.07, causal=0):
+        return na(ql, ctypes.byref(kv), B, s_q, H, scale, causal, o, o_dtype, None, None)
+
+    assert call(_kv(), ql=None) == ARG
+    assert call(_kv(), o=None) == ARG
+    assert call(_kv(), o_dtype=1) == ARG
+    assert call(_kv(), causal=3) == ARG
+    assert call(_kv(max_seqlen=4), s_q=5) == ARG
+    assert call(_kv(block_table=0x7000, block_size=32, max_blocks=8)) == UNSUP
+    big = _kv(T_stride=4096, max_seqlen=4096)
+    assert m._lib.mla_decode_workspace_bytes(64, 1, 128, 4096) > cap
+    assert call(big, B=64, H=128) == WS
