@@ -106,6 +106,43 @@ def copy_calibration(steps: int):
                       "us_per_launch": round(us, 2), "copy_gbs": round(2 * COPY_BYTES / us / 1e3, 1)}), flush=True)
 
 
+def blas_info(pools):
+    """The BLAS library numpy runs on (vendor, version, threads in use)."""
+    blas = [p for p in pools if p.get("user_api") == "blas"] or list(pools)
+    if not blas:
+        return {"vendor": "unknown", "threads": 1}
+    b = blas[0]
+    return {"vendor": b.get("internal_api", "unknown"), "version": b.get("version"),
+            "threads": int(b.get("num_threads", 1))}
+
+
+def measured_peaks(dev):
+    """Achievable peaks measured on this GPU: HBM bandwidth of a plain copy
+    (read + write of 1 GiB) and dense bf16 matrix throughput of an
+    8192^3 library GEMM; the roofline fractions are also quoted against
+    these."""
+    import torch
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    out = {}
+    for name, fn, work in (("hbm_copy_gbs", lambda: dst.copy_(src), 2 * COPY_BYTES / 1e9),
+                           ("bf16_gemm_tflops", lambda: torch.mm(a, b), 2 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(work * 10 / (e0.elapsed_time(e1) * 1e-3), 1)
+    del src, dst, a, b
+    return out
+
+
 def cpu_baseline(inp, scale, seconds_target=15.0, selection=None):
     """The fp64 oracle (naive expand-then-attend) on a bounded sample of (b, h)
     pairs of the same workload, scaled to the step's metric: the absorbed-path
@@ -130,11 +167,13 @@ def cpu_baseline(inp, scale, seconds_target=15.0, selection=None):
             flops += vis * (2 * 576 + 2 * 512) + 2 * 2 * 128 * 512 * w.s_q
         done += len(pairs)
     dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    blas = blas_info(threadpool_info())
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": threads,
+        "cores": blas["threads"],
+        "host_cores": len(os.sched_getaffinity(0)),
+        "blas": blas,
         "kind": "oracle",
         "sample": f"{done} random (sequence, head) pairs of the {w.name} workload (B={w.B} H={w.H} "
                   f"s_q={w.s_q} T={w.T or w.T_range}{'' if selection is None else f' top-{w.topk}'}), "
@@ -251,7 +290,8 @@ def append_main(args, w):
         dt = time.perf_counter() - t_start
         rec["cpu_baseline"] = {
             "value": round(done * alg_bytes / dt / 1e9, 3), "unit": "GB/s",
-            "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1]), "kind": "oracle",
+            "cores": blas_info(threadpool_info())["threads"], "host_cores": len(os.sched_getaffinity(0)),
+            "blas": blas_info(threadpool_info()), "kind": "oracle",
             "sample": f"{done} full calls of the fp64 numpy latent-append oracle on the same {w.N} tokens, {dt:.1f} s",
         }
     print(json.dumps(rec), flush=True)
@@ -349,7 +389,8 @@ def prefill_main(args, w):
         dt = time.perf_counter() - t_start
         rec["cpu_baseline"] = {
             "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": max([i.get("num_threads", 1) for i in threadpool_info()] or [1]), "kind": "oracle",
+            "cores": blas_info(threadpool_info())["threads"], "host_cores": len(os.sched_getaffinity(0)),
+            "blas": blas_info(threadpool_info()), "kind": "oracle",
             "sample": f"{done} random (sequence, head) pairs of the {w.name} workload, fp64 numpy expand-then-attend, "
                       f"{dt:.1f} s; value = expand-path FLOPs of those pairs per second",
         }
@@ -432,7 +473,7 @@ def main():
 
     PART_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}[PART_DTYPE_NAME]
 
-    def step(i, ev=None):
+    def step(i, ev=None, part_dtype=PART_DTYPE):
         c = caches[i % N_COPIES]
         if ev is not None:
             ev[0].record(stream)
@@ -440,14 +481,19 @@ def main():
         if ev is not None:
             ev[1].record(stream)
         if sparse:
-            mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws, part_dtype=PART_DTYPE)
+            mla.sparse_decode_partial(q_lat, c, sel_idx, sel_count, scale, workspace=ws, part_dtype=part_dtype)
         else:
-            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws, fp8_math=f8m, part_dtype=PART_DTYPE)
+            mla.decode_partial(q_lat, c, scale, w.causal, workspace=ws, fp8_math=f8m, part_dtype=part_dtype)
         if ev is not None:
             ev[2].record(stream)
-        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1), part_dtype=PART_DTYPE)
+        mla.decode_combine_out(ws, w_uv, B, s_q, H, scan_len, out=out.view(N, H, -1), part_dtype=part_dtype)
         if ev is not None:
             ev[3].record(stream)
+
+    def keep_host_ahead():
+        # a short spin on the GPU lets the host queue the next launches before
+        # the GPU reaches them, so that no timed span holds host launch time
+        torch.cuda._sleep(2_000_000)
 
     for i in range(args.warmup):
         step(i)
@@ -460,6 +506,7 @@ def main():
     n_timed = args.steps
     if not args.graph:
         torch.cuda.synchronize()
+        keep_host_ahead()
         t0.record(stream)
         for i in range(args.steps):
             step(i)
@@ -473,6 +520,7 @@ def main():
         torch.cuda.synchronize()
         reps = max(1, -(-args.steps // N_COPIES))
         n_timed = reps * N_COPIES
+        keep_host_ahead()
         t0.record(stream)
         for _ in range(reps):
             graph.replay()
@@ -480,22 +528,47 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / n_timed
 
-    # per-kernel durations with HIP events on the launch stream (recorded
-    # back to back, read after one synchronisation)
+    # statistics pass: at least 50 steps with HIP events on the launch stream
+    # at every kernel boundary (recorded back to back, read after one
+    # synchronisation): per-step median / p10 / p90 and per-kernel durations
     fused_gather = sparse and not cache0.paged and not cache0.fp8
     scan_name = ("decode_split (gather fused)" if fused_gather else "sparse_gather+decode_split") if sparse \
         else "decode_split"
     names = ["absorb_q", scan_name, "combine_out"]
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    n_stats = max(args.steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_stats)]
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    keep_host_ahead()
+    for i in range(n_stats):
         step(i, evs[i])
     torch.cuda.synchronize()
-    tot = [0.0] * len(names)
-    for i in range(args.steps):
-        for k in range(len(names)):
-            tot[k] += evs[i][k].elapsed_time(evs[i][k + 1])
-    kern_us = {n: 1e3 * t / args.steps for n, t in zip(names, tot)}
+    spans = {n: [evs[i][k].elapsed_time(evs[i][k + 1]) * 1e3 for i in range(n_stats)] for k, n in enumerate(names)}
+    step_ms = [evs[i][0].elapsed_time(evs[i][len(names)]) for i in range(n_stats)]
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+    kern_us = {n: sum(v) / len(v) for n, v in spans.items()}
+    step_stats = {"steps": n_stats, "median_ms": round(pct(step_ms, 0.5), 5), "p10_ms": round(pct(step_ms, 0.1), 5),
+                  "p90_ms": round(pct(step_ms, 0.9), 5),
+                  "kernel_median_us": {n: round(pct(v, 0.5), 2) for n, v in spans.items()},
+                  "kernel_p10_us": {n: round(pct(v, 0.1), 2) for n, v in spans.items()},
+                  "kernel_p90_us": {n: round(pct(v, 0.9), 2) for n, v in spans.items()}}
+
+    # the same step with fp32 split partials (the scope's default precision)
+    if True:
+        torch.cuda.synchronize()
+        for i in range(3):
+            step(i, part_dtype=torch.float32)
+        torch.cuda.synchronize()
+        keep_host_ahead()
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i, part_dtype=torch.float32)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        fp32_step_ms = t0.elapsed_time(t1) / args.steps
 
     fp8 = w.cache_dtype == "fp8"
     peak_mfma = FP8_PEAK_TFLOPS if f8m else BF16_PEAK_TFLOPS
@@ -524,9 +597,16 @@ def main():
         "algorithmic_bytes_per_launch": cnt["bytes_scan"],
         "algorithmic_flops_per_launch": cnt["flops_scan"],
         "avg_launch_us": round(kern_us[names[1]], 2),
+        "median_launch_us": step_stats["kernel_median_us"][names[1]],
         "achieved_tflops": round(scan_tflops, 1),
         "achieved_gbs": round(scan_gbs, 1),
     }
+    peaks = measured_peaks(dev)
+    meas = peaks["hbm_copy_gbs"] if hbm_bound else (None if f8m else peaks["bf16_gemm_tflops"])
+    roofline["peak_measured"] = meas
+    roofline["peak_measured_how"] = ("1 GiB device copy (read + write)" if hbm_bound
+                                     else None if f8m else "8192^3 bf16 library GEMM")
+    roofline["frac_of_measured"] = round(roofline["achieved"] / meas, 4) if meas else None
     rec = {
         "metric": "absorbed MLA decode TFLOP/s + HBM GB/s (% roofline), H=128 B=64 T=4096",
         "value": round(tflops, 2),
@@ -549,6 +629,9 @@ def main():
         "step_gbs": round(cnt["bytes_step"] / s / 1e9, 1),
         "tokens_per_s": round(N / s, 1),
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "step_stats": step_stats,
+        "ms_per_step_fp32_partials": round(fp32_step_ms, 5),
+        "measured_peaks": peaks,
         "roofline": roofline,
     }
     if args.naive_steps > 0 and not sparse:
@@ -566,10 +649,15 @@ def main():
         naive_ms = n0.elapsed_time(n1) / args.naive_steps
         naive_flops = cnt["flops_scan"] // (2 * 576 + 2 * 512) * (2 * 192 + 2 * 128) + \
             sum(int(x) for x in inp["seqlens"]) * H * 2 * (2 * 512 * 128)
+        naive_tflops = naive_flops / (naive_ms * 1e-3) / 1e12
         rec["naive_ablation"] = {
             "ms_per_step": round(naive_ms, 4),
             "absorbed_speedup": round(naive_ms / ms_per_step, 2),
-            "naive_algorithmic_tflops": round(naive_flops / (naive_ms * 1e-3) / 1e12, 1),
+            "naive_algorithmic_tflops": round(naive_tflops, 1),
+            # the speedup says little unless read beside how close the naive
+            # kernel itself runs to its own (bf16 MFMA) roofline
+            "naive_frac_of_bf16_peak": round(naive_tflops / BF16_PEAK_TFLOPS, 4),
+            "flop_ratio_naive_over_absorbed": round(naive_flops / cnt["flops_scan"], 1),
             "naive_flops": naive_flops,
         }
     if not args.no_cpu_baseline:
