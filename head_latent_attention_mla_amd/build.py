@@ -29,13 +29,20 @@ FLAGS = [
 ]
 
 
+# per-source flags: the decode scan with score and value waves keeps every
+# MFMA operand in VGPRs, so its two kinds of waves share one pool of 256
+# registers (by default the budget is split evenly between VGPRs and AGPRs,
+# and neither the latent queries nor the accumulators fit a half)
+FILE_FLAGS = {"mla_decode_sv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -31,12 +31,15 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 
 // Pick this work-group's (sequence b, part j of parts, partial slot sl, row
 // group g).  Returns false for a surplus work-group (uniform per work-group),
-// which must exit.  lds_scratch: PLAN_SCRATCH_BYTES of LDS, free on entry and
-// on return.  The first work-group of a sequence records where its partials
-// are (seg_first / seg_count).
-__device__ __forceinline__ bool plan_work(const DecodeParams& p, int64_t* lds_scratch, int& b, int& j, int& parts,
-                                          int& sl, int& g) {
-  constexpr int NTHREADS = PLAN_THREADS;
+// which must exit.  NT: threads of the work-group (a multiple of 64, at most
+// 1024); lds_scratch: (2 NT + 4) * 8 bytes of LDS, free on entry and on
+// return.  The first work-group of a sequence records where its partials are
+// (seg_first / seg_count).
+template <int NT>
+__device__ __forceinline__ bool plan_work_t(const DecodeParams& p, int64_t* lds_scratch, int& b, int& j,
+                                            int& parts, int& sl, int& g) {
+  constexpr int NTHREADS = NT;
+  constexpr int NWAVES = NT / 64;
   constexpr int KT = PLAN_TILE;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -48,15 +51,15 @@ __device__ __forceinline__ bool plan_work(const DecodeParams& p, int64_t* lds_sc
   // partial slots Qp[b] .. Qp[b] + parts(b) - 1 (Qp: prefix sum of parts),
   // fewer than n_ranges + B in all.  Every work-group derives the same plan
   // from the sequence lengths (chunked sums and two inclusive scans over the
-  // 256 chunks), then takes one (slot, row group) pair; the blockIdx -> pair
-  // map puts consecutive slots on one XCD (shared L2) and the surplus
-  // work-groups of the launch at its end.
+  // NT chunks), then takes one (slot, row group) pair; the blockIdx -> pair
+  // map puts consecutive slots (and the row groups of a slot) on one XCD
+  // (shared L2) and the surplus work-groups of the launch at its end.
   {
-    int64_t* scan = lds_scratch;           // 2 x 256 entries
+    int64_t* scan = lds_scratch;           // 2 x NT entries
     int64_t* found = scan + 2 * NTHREADS;  // the slot's sequence and its first slot
     const int chunk = (p.B + NTHREADS - 1) / NTHREADS;
     const int c0 = min(p.B, tid * chunk), c1 = min(p.B, c0 + chunk);
-    // inclusive prefix over the 256 threads: shuffle scan within each wave,
+    // inclusive prefix over the NT threads: shuffle scan within each wave,
     // then the wave totals through LDS; found[2] receives the grand total
     auto inclusive_scan = [&](int64_t mine) -> int64_t {
       int64_t v = mine;
@@ -67,9 +70,12 @@ __device__ __forceinline__ bool plan_work(const DecodeParams& p, int64_t* lds_sc
       }
       if (lane == 63) scan[wave] = v;
       __syncthreads();
-      int64_t before = 0;
-      for (int w2 = 0; w2 < wave; ++w2) before += scan[w2];
-      const int64_t all = scan[0] + scan[1] + scan[2] + scan[3];
+      int64_t before = 0, all = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NWAVES; ++w2) {
+        before += w2 < wave ? scan[w2] : 0;
+        all += scan[w2];
+      }
       __syncthreads();
       found[2] = all;
       return v + before;
@@ -118,6 +124,11 @@ __device__ __forceinline__ bool plan_work(const DecodeParams& p, int64_t* lds_sc
     }
   }
   return true;
+}
+
+__device__ __forceinline__ bool plan_work(const DecodeParams& p, int64_t* lds_scratch, int& b, int& j, int& parts,
+                                          int& sl, int& g) {
+  return plan_work_t<PLAN_THREADS>(p, lds_scratch, b, j, parts, sl, g);
 }
 
 }  // namespace mla
