@@ -29,11 +29,8 @@ FLAGS = [
 ]
 
 
-# per-source flags: the decode scan with score and value waves keeps every
-# MFMA operand in VGPRs, so its two kinds of waves share one pool of 256
-# registers (by default the budget is split evenly between VGPRs and AGPRs,
-# and neither the latent queries nor the accumulators fit a half)
-FILE_FLAGS = {"mla_decode_sv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# per-source flags (none at present)
+FILE_FLAGS = {}
 
 
 def sources():

@@ -12,8 +12,7 @@
 
 namespace {
 
-constexpr int kRowsPerGroup = 128;   // query rows per work-group of the FP8 and sparse scans
-constexpr int kRowsPerGroupSV = 64;  // query rows per work-group of the bf16 scan (score + value waves)
+constexpr int kRowsPerGroup = 128;   // query rows per work-group of the split-T scans
 constexpr int kTileRows = 64;        // cached rows per plan tile
 constexpr int kTargetWorkGroups = 256;  // one work-group per compute unit of an MI355X
 constexpr size_t kAlign = 256;
@@ -32,31 +31,21 @@ struct Plan {
 // tiles of all sequences into n_ranges = B * n_split equal ranges, so shorter
 // sequences get proportionally fewer parts.  A range covers at most one part
 // per sequence it touches: at most n_ranges + B partial slots.
-// rows_per_group: query rows per work-group of the scan that will run.  The
-// workspace is laid out for 128-row groups, which give the most parts (fewer
-// row groups, more splits to fill the device), so one layout -- and the
-// merge kernels' offsets -- serves every scan.
-bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t forced, Plan* pl,
-               int32_t rows_per_group = kRowsPerGroup) {
+bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t forced, Plan* pl) {
   if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || forced < 0) return false;
   const int64_t R = (int64_t)s_q * H;
   if (R > (1 << 24) || B > (1 << 20) || max_seqlen > (1 << 28)) return false;
   pl->R = (int32_t)R;
   const int64_t tiles = (max_seqlen + kTileRows - 1) / kTileRows;
-  auto splits = [&](int64_t groups) {
-    const int64_t base = (int64_t)B * groups;
-    int64_t ns = forced > 0 ? forced : (kTargetWorkGroups + base - 1) / base;
-    if (ns < 1) ns = 1;
-    if (ns > tiles) ns = tiles;
-    return ns;
-  };
-  const int64_t groups_layout = (R + kRowsPerGroup - 1) / kRowsPerGroup;
-  pl->n_slots = (int64_t)B * splits(groups_layout) + B;
-  pl->n_groups = (int32_t)((R + rows_per_group - 1) / rows_per_group);
-  const int64_t ns = splits(pl->n_groups);
+  pl->n_groups = (int32_t)((R + kRowsPerGroup - 1) / kRowsPerGroup);
+  const int64_t base = (int64_t)B * pl->n_groups;
+  int64_t ns = forced > 0 ? forced : (kTargetWorkGroups + base - 1) / base;
+  if (ns < 1) ns = 1;
+  if (ns > tiles) ns = tiles;
   pl->n_split = (int32_t)ns;
   const int64_t n_ranges = (int64_t)B * ns;
-  const int64_t n_work = (n_ranges + B) * pl->n_groups;   // one work-group per (slot, row group)
+  pl->n_slots = n_ranges + B;
+  const int64_t n_work = pl->n_slots * pl->n_groups;   // one work-group per (slot, row group)
   if (n_work > (int64_t)1 << 30) return false;
   pl->n_ranges = (int32_t)n_ranges;
   pl->n_work = (int32_t)n_work;
@@ -271,17 +260,6 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   if (fp8_math) {
     if (!p.fp8) return MLA_ERR_UNSUPPORTED;
     return hip_status(mla::launch_decode_split_f8(p, st));
-  }
-  if (!p.fp8 && sel_idx == nullptr) {
-    // bf16 cache: the scan with score and value waves, 64 query rows per
-    // work-group (same workspace layout and partial format)
-    Plan sv;
-    if (!make_plan(B, s_q, H, plan_len, num_splits, &sv, kRowsPerGroupSV)) return MLA_ERR_ARG;
-    p.n_groups = sv.n_groups;
-    p.n_ranges = sv.n_ranges;
-    p.n_work = sv.n_work;
-    p.work_per_xcd = sv.work_per_xcd;
-    return hip_status(mla::launch_decode_sv(p, st));
   }
   return hip_status(mla::launch_decode_split(p, st));
 }

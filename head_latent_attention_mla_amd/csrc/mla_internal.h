@@ -30,7 +30,7 @@ struct DecodeParams {
   int64_t T_stride;
   int32_t max_blocks;
   int32_t B, s_q, H, R;
-  int32_t n_groups;             // row groups per sequence (ceil(R / rows per work-group))
+  int32_t n_groups;             // ceil(R / 128) row groups per sequence
   int32_t n_ranges;             // equal ranges of the tiles of all sequences
   int32_t n_work, work_per_xcd; // n_ranges * n_groups work items over 8 XCDs
   float scale_log2;             // softmax scale * log2(e)
@@ -138,7 +138,6 @@ constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
 hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_decode_split(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_sv(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_split_f8(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 // part_o: fp32 partials, or bf16 when part_bf16 is set
