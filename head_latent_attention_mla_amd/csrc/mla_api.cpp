@@ -22,7 +22,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int32_t R, n_groups, n_split, n_ranges, n_work, work_per_xcd;
   int64_t n_slots;
-  size_t part_o_bytes, part_lse_bytes, seg_bytes, ws_bytes;
+  size_t part_o_bytes, part_lse_bytes, seg_bytes, mrun_bytes, ws_bytes;
 };
 
 // The plan depends on host integers only, so the workspace size and the
@@ -53,7 +53,9 @@ bool make_plan(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen, int32_t fo
   pl->part_o_bytes = align_up((size_t)pl->n_slots * R * mla::D_C * sizeof(float));
   pl->part_lse_bytes = align_up((size_t)pl->n_slots * R * sizeof(float));
   pl->seg_bytes = align_up((size_t)2 * B * sizeof(int32_t));
-  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes + pl->seg_bytes;
+  // per-part maximum scores of the FP8-arithmetic scan (its accuracy check)
+  pl->mrun_bytes = pl->part_lse_bytes;
+  pl->ws_bytes = pl->part_o_bytes + pl->part_lse_bytes + pl->seg_bytes + pl->mrun_bytes;
   return true;
 }
 
@@ -259,7 +261,14 @@ mla_status decode_partial_impl(const void* q_lat, const mla_kv_desc* kv, int32_t
   }
   if (fp8_math) {
     if (!p.fp8) return MLA_ERR_UNSUPPORTED;
-    return hip_status(mla::launch_decode_split_f8(p, st));
+    // E4M3 arithmetic, then the bf16-arithmetic scan over the (sequence, row
+    // group) pairs holding a row it cannot resolve to the FP8 bar (a peaked
+    // softmax or few rows)
+    p.part_mrun = (float*)((char*)workspace + pl.part_o_bytes + pl.part_lse_bytes + pl.seg_bytes);
+    const hipError_t e = mla::launch_decode_split_f8(p, st);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    p.fixup = 1;
+    return hip_status(mla::launch_decode_split(p, st));
   }
   return hip_status(mla::launch_decode_split(p, st));
 }

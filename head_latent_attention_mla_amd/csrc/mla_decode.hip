@@ -188,6 +188,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       p.seg_count[b] = parts;
     }
   }
+  if (p.fixup) {
+    // fix-up after the FP8-arithmetic scan (same plan): with E4M3 queries and
+    // weights a row stays within the FP8 bar while its largest probability is
+    // at most 1/32 of its total; recompute this (sequence, row group) only if
+    // one of its rows passes that, i.e. max over parts of the part maxima
+    // against the merged log-sum-exp (log2 domain) exceeds -5
+    bool peaked = false;
+    if (tid < 128 && g * 128 + tid < p.R) {
+      const int64_t row = g * 128 + tid;
+      const int s0 = p.seg_first[b], ns = p.seg_count[b];
+      float m = -INFINITY, lmax = -INFINITY;
+      for (int s = 0; s < ns; ++s) {
+        m = fmaxf(m, p.part_mrun[(s0 + s) * (int64_t)p.R + row]);
+        lmax = fmaxf(lmax, p.part_lse[(s0 + s) * (int64_t)p.R + row]);
+      }
+      float sum = 0.f;
+      for (int s = 0; s < ns; ++s) {
+        const float l = p.part_lse[(s0 + s) * (int64_t)p.R + row];
+        sum += l == -INFINITY ? 0.f : exp2f(l - lmax);
+      }
+      peaked = sum > 0.f && m - (lmax + log2f(sum)) > -5.0f;
+    }
+    // any row of the work-group: one word per wave in the idle probability buffer
+    int* const any = (int*)pbuf;
+    const bool wave_any = __builtin_amdgcn_ballot_w64(peaked) != 0;
+    if (lane == 0) any[wave] = wave_any ? 1 : 0;
+    __syncthreads();
+    const int flagged = any[0] | any[1] | any[2] | any[3];
+    __syncthreads();                         // the buffer is reused below
+    if (flagged == 0) return;                // uniform per work-group
+  }
   const int nt_b = (seq_len(b) + KT - 1) / KT;
   const int T = seq_len(b);
   const int t_begin = (int)floor_div((int64_t)j * nt_b, parts) * KT;

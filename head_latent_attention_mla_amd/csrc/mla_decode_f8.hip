@@ -15,6 +15,11 @@
 //            w = p * sigma_t * 2^-e, quantised to E4M3; the row normaliser sums
 //            the weights actually used, dequant(w8) / (sigma_t 2^-e), so a row
 //            of few cached rows stays normalised
+// A query row whose largest probability is more than 1/32 of its total (few
+// rows, or a peaked softmax) does not average out the E4M3 rounding of its
+// weights and query: each part records its rows' maximum scores, and the
+// bf16-arithmetic scan then recomputes the (sequence, row group) pairs that
+// hold such a row.
 // q8 = E4M3(q_lat / qscale_row), qscale_row = amax|q_lat row| / 448.  The
 // exponent e is this work-group's running max of ceil(log2 sigma), so w <= 2^8
 // (the softmax reference moves in steps of 2^8 here); when it grows the
@@ -220,6 +225,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     for (int k = 0; k < 4; ++k) acc[i][k] = f32x16{};
   float m_ref = -INFINITY;
   float l_sum = 0.f;
+  float m_run = -INFINITY;   // running maximum of the row's scaled scores (log2 domain)
   int e_cur = E_NONE;
 
   float sc_next = 0.f;
@@ -333,6 +339,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
         mq[c] = max3f(m, x1[r + 1], fmaxf(x1[r + 2], x1[r + 3]));
       }
       const float mx = max_halves(fmaxf(max3f(mq[0], mq[1], mq[2]), mq[3])) * c_row;
+      m_run = fmaxf(m_run, mx);
       const bool first = m_ref == -INFINITY;
       const float over = (mx - m_ref - REF_STEP) * (1.0f / REF_STEP);
       const int kraw = (!first && over > 0.f) ? (int)ceilf(over) : 0;
@@ -447,6 +454,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
   const int64_t pbase = (int64_t)sl * p.R;
   store_split_partials(p, acc, lsh, smem, pbase, g, wave, lane, unscale);
   if (half == 0 && own_ok) p.part_lse[pbase + own_r] = l_sum > 0.f ? m_ref + log2f(l_sum) : -INFINITY;
+  // the part's maximum score, for the accuracy check of the fix-up scan
+  if (half == 0 && own_ok && p.part_mrun != nullptr) p.part_mrun[pbase + own_r] = m_run;
 }
 
 }  // namespace

@@ -43,6 +43,15 @@ struct DecodeParams {
   const int32_t* src_len;       // [B] cache lengths
   int32_t k_max;
   int32_t part_bf16;            // partial outputs stored as bf16 (else fp32)
+  // FP8-arithmetic scan: fp32 [n_slots, R], each part's running maximum of
+  // every query row's scaled scores (log2 domain, like part_lse); null: not
+  // written
+  float* part_mrun;
+  // bf16-arithmetic scan run as a fix-up after the FP8-arithmetic one: a
+  // (sequence, row group) is recomputed only if one of its query rows has a
+  // largest probability above 1/32 of the row's total (max over parts of
+  // part_mrun against the merged log-sum-exp); the rest exit after the plan
+  int32_t fixup;
 };
 
 // One call of the naive (expand-then-attend) ablation.

@@ -214,7 +214,11 @@ mla_status mla_decode_attn_noalloc(const void* q_lat, const mla_kv_desc* kv,
  *               no visible row);
  *     seg_first int32 [B], then seg_count int32 [B], at aligned(...) after
  *               part_lse: sequence b's parts are the slots seg_first[b] ..
- *               seg_first[b] + seg_count[b] - 1, in row order.
+ *               seg_first[b] + seg_count[b] - 1, in row order;
+ *     part_mrun fp32 [M, R] at aligned(...) after the seg tables: each
+ *               part's maximum scaled score per row (log2 domain), written
+ *               by mla_decode_partial_fp8 for its accuracy check (unused by
+ *               the other calls).
  *   The offsets do not depend on part_dtype (bf16 partials use the first half
  *   of the part_o region).  Slots outside every sequence's run are left
  *   unwritten.
@@ -274,9 +278,14 @@ mla_status mla_decode_combine_out(int32_t B, int32_t s_q, int32_t H, int32_t max
  * MLA_FP8_E4M3 (else MLA_ERR_UNSUPPORTED).  The cached codes enter the matrix
  * products as they are; each latent query row is quantised to E4M3 with its
  * own scale amax/448, and the softmax weights times the row scales to E4M3
- * (against a power-of-two normaliser), so the result approximates the exact
- * attention to FP8 precision: about 1e-2 absolute on unit-scale outputs,
- * within the FP8 bar of 6e-2. */
+ * (against a power-of-two normaliser).  That is accurate to the FP8 bar
+ * (6e-2 absolute on unit-scale outputs) only where many comparable weights
+ * average out the E4M3 rounding.  The scan records each part's maximum
+ * score per row; the call then runs the bf16-arithmetic scan as a fix-up
+ * that recomputes (and overwrites the partials of) every (sequence, row
+ * group) holding a query row whose largest probability exceeds 1/32 of the
+ * row's total (few visible rows, or a peaked softmax).  Where no row does,
+ * that second scan exits after its work plan. */
 mla_status mla_decode_partial_fp8(const void* q_lat, const mla_kv_desc* kv, int32_t B,
                                   int32_t s_q, int32_t H, float softmax_scale, int32_t causal,
                                   void* workspace, size_t ws_bytes, int32_t num_splits,

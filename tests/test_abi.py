@@ -71,12 +71,13 @@ def test_workspace_and_split_plan(m):
     # DeepSeek-V3 shape: 64 sequences x 1 row group -> 4 parts of 1024 rows each;
     # B * (S + 1) = 320 partial slots of 128 rows, then the two [B] int32 tables
     assert ns(64, 1, 128, 4096, 0) == 4
-    assert ws(64, 1, 128, 4096, 0) == 320 * 128 * 512 * 4 + 320 * 128 * 4 + 512
+    # + the FP8-arithmetic scan's per-part row maxima (as large as part_lse)
+    assert ws(64, 1, 128, 4096, 0) == 320 * 128 * 512 * 4 + 2 * 320 * 128 * 4 + 512
     assert ns(32, 4, 128, 8192, 0) == 2
     assert ns(16, 1, 128, 32768, 0) == 16     # ragged batches: 256 ranges over all tiles
     assert ns(2, 1, 16, 256, 0) == 4          # capped by the number of 64-row tiles
     assert ns(2, 1, 16, 256, 3) == 3
-    assert ws(2, 1, 16, 256, 3) == 2 * 4 * 16 * 512 * 4 + 8 * 16 * 4 + 256
+    assert ws(2, 1, 16, 256, 3) == 2 * 4 * 16 * 512 * 4 + 2 * 8 * 16 * 4 + 256
     assert ns(1, 1, 128, 1, 0) == 1
     assert ws(0, 1, 128, 100, 0) == 0 and ws(1, 1, 128, 0, 0) == 0 and ws(1, 1, 128, 10, -1) == 0
 
