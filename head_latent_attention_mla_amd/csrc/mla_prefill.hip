@@ -6,10 +6,10 @@
 //
 // The expansion writes K_nope and V token-major, [B, T_pad, H * 128 + 64]
 // bf16 (head h at h * 128 of a row; the pad keeps one head's rows from being
-// a power of two apart): expand_kv_kernel, one persistent work-group per
-// (head, K or V) that holds that half of the head's weights in LDS and
-// streams every cached row (contiguous or paged, bf16 or dequantised E4M3)
-// through MFMA, rows past a sequence's end written as 0.
+// a power of two apart): expand_kv_kernel, one work-group per (head, K or V)
+// that holds that half of the head's weights in registers and streams every
+// cached row (contiguous or paged, bf16 or dequantised E4M3) through LDS into
+// MFMA, rows past a sequence's end written as 0.
 //   copy_rope_kernel copies the rows' rope keys to [B, T_pad, 64].
 // Rows past a sequence's end are masked in the attention.  Then one
 // attention kernel:
@@ -32,7 +32,7 @@ namespace {
 
 constexpr int KT = 64;                        // cached rows per attention tile
 constexpr int QT = 128;                       // query rows per attention work-group
-constexpr int ET = 128;                       // cached rows per expansion work-group
+constexpr int ET = 128;                       // cached rows per rope-copy work-group
 constexpr int KN_BYTES = KT * D_NOPE * 2;     // 16 KB: K_nope tile
 constexpr int KR_BYTES = KT * D_ROPE * 2;     // 8 KB: rope key tile
 constexpr int V_BYTES = KT * D_V * 2;         // 16 KB: V tile
@@ -63,149 +63,197 @@ __device__ __forceinline__ void dequant16(u32x4 w, float s, i16x8& lo, i16x8& hi
 }
 
 // ---------------------------------------------------------------------------
-// expansion: one persistent work-group per (head, K or V) keeps that half of
-// the head's weights -- W_UK[h] or W_UV[h]^T, 128 rows x 512 -- in LDS (128
-// KB, 16-byte chunks XOR row & 7) and walks every 128-row tile of every
-// sequence: D[n][t] = sum_c W[n][c] C[t][c], K = 512 in 8 chunks of 64.  Wave
-// (nq, tq) = (w & 1, w >> 1) owns outputs 64 nq .. + 63 and tile rows 64 tq ..
-// + 63 (2 x 2 blocks of 32 x 32).  The cached-row fragments go straight to
-// registers, three chunks ahead across tile boundaries; within a chunk the k
-// order is permuted alike for both operands (lane half h holds c = 32 h ..
-// 32 h + 31, MFMA j takes 8 j .. 8 j + 7), so a lane reads 64 contiguous bytes.
+// expansion: one work-group per (head, K or V), one per compute unit.  Its
+// weight half -- W_UK[h] or W_UV[h]^T, 128 outputs x 512 -- stays in registers
+// as MFMA A fragments (wave w: outputs 32 w .. 32 w + 31, 128 VGPRs a lane).
+// The cached rows stream through LDS in 64-row tiles, double-buffered, each
+// direct-to-LDS load filling one whole 1 KB row (16-byte chunk c of row t at
+// slot c ^ (t & 15), so the fragment reads of 16 consecutive rows hit
+// distinct banks): D[n][t] = sum_c W[n][c] C[t][c] in 32 k-steps of 16, every
+// C fragment read from LDS once.  A tile's 128 x 64 result is staged in LDS
+// and stored one tile later as whole 256-byte row pieces.  E4M3 rows: the
+// codes land in LDS and are converted (code x row scale -> bf16) into a
+// single bf16 tile buffer at the top of the tile.
 // ---------------------------------------------------------------------------
-constexpr int E_AHEAD = 3;                      // chunks of cached-row fragments in flight
-constexpr int E_NCH = D_C / 64;                 // 8 chunks of 64 per tile
+constexpr int X_T = 64;                         // cached rows per tile
+constexpr int X_TILE = X_T * D_C * 2;           // 64 KB: bf16 tile, 1 KB rows
+constexpr int X_CODES = X_T * D_C;              // 32 KB: e4m3 codes of a tile
+constexpr int X_STAGE = X_T * D_NOPE * 2;       // 16 KB: a tile's outputs, 256-byte rows
+constexpr int X_RING = 4;                       // k-steps of C fragments in flight
+static_assert(2 * X_TILE + 2 * X_STAGE <= 160 * 1024, "LDS budget");
+static_assert(X_TILE + 2 * X_CODES == 2 * X_TILE, "E4M3 layout fits the bf16 one");
+
+template <int OFF>
+__device__ __forceinline__ void lds_write_b64(uint32_t addr, uint64_t v) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset");
+  asm volatile("ds_write_b64 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
 
 template <bool FP8>
-__global__ __launch_bounds__(256) void expand_kv_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char wl[D_NOPE * D_C * 2];   // 128 KB
+__global__ __launch_bounds__(256, 1) void expand_kv_kernel(PrefillParams p) {
+  // bf16 rows: tile buffers 0 and 1; E4M3 rows: the bf16 tile, then two code
+  // buffers; then two output staging buffers
+  __shared__ __attribute__((aligned(1024))) char smem[2 * X_TILE + 2 * X_STAGE];
+  const uint32_t smem_a = lds_addr(smem);
+  const uint32_t stage_a = smem_a + 2 * X_TILE;
   const int h = blockIdx.x >> 1, part = blockIdx.x & 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int nq = wave & 1, tq = wave >> 1;
-  const uint32_t wl_a = lds_addr(wl);
+  const int n_tt = p.T_pad / X_T;
+  const int n_tiles = p.B * n_tt;
+  if (n_tiles == 0) return;
 
-  // the weight half: row L of 1 KB is load L (wave w: rows 32 w .. + 31);
-  // slot lane holds logical chunk lane ^ (L & 7)
-  {
-    const uint16_t* W = (part ? p.w_uvt : p.w_uk) + (int64_t)h * D_NOPE * D_C;
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      const int L = 32 * wave + i;
-      __builtin_amdgcn_global_load_lds((const void*)(W + (int64_t)L * D_C + 8 * (lane ^ (L & 7))),
-                                       (lds_void_t*)(wl + L * 1024), 16, 0, 0);
-    }
-  }
-  // A-fragment reads: row 64 nq + 32 nb + l32, logical chunk 8 ch + 4 half + j
-  uint32_t wo[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) wo[j] = wl_a + (64 * nq + l32) * 1024 + 16 * ((4 * half + j) ^ (l32 & 7));
-
-  const int n_tt = p.T_pad / ET;
-  const int n_steps = p.B * n_tt * E_NCH;
-  constexpr int elem = FP8 ? 1 : 2;
-  // the cached row behind fragment (step s, t-block tb) of this lane; rows
-  // past a sequence's end reuse its last row (their outputs are stored as 0)
-  auto frag_src = [&](int s, int tb, float& sc) -> const char* {
-    const int tile = s / E_NCH, ch = s % E_NCH;
-    const int b = tile / n_tt, tt = tile % n_tt;
-    const int T = p.seqlens[b];
-    const int t = min(tt * ET + 64 * tq + 32 * tb + l32, T - 1);
-    const int64_t r = cache_row(p, b, t);
-    sc = FP8 ? p.row_scale[r] : 1.0f;
-    return (const char*)p.rows + (r * ROWW + ch * 64 + 32 * half) * elem;
+  constexpr int ELEM = FP8 ? 1 : 2;
+  constexpr int ROW_BYTES = ROWW * ELEM;
+  // tile `it` = (sequence b, rows t0 .. t0 + 63).  Its sequence length and
+  // block-table entry are loaded one tile before the tile's loads are issued
+  // and only then moved to scalar registers, so that no load waits on them
+  // right after they were fetched.
+  int meta_len = 0, meta_blk = 0;
+  auto load_meta = [&](int it) {
+    const int b = it / n_tt, t0 = (it % n_tt) * X_T;
+    meta_len = p.seqlens[b];
+    if (p.block_table != nullptr)   // an in-range entry; unused for a tile past the sequence's end
+      meta_blk = p.block_table[(int64_t)b * p.max_blocks + min(t0 >> 6, p.max_blocks - 1)];
   };
-  // ring of fragments (bf16 rows) or raw codes and scales (e4m3 rows)
-  i16x8 cf[E_AHEAD + 1][2][FP8 ? 1 : 4];
-  float csc[E_AHEAD + 1][2];
-  uint32_t c8[E_AHEAD + 1][2][FP8 ? 8 : 1];
-  auto issue = [&](int s, auto slotc) {
-    constexpr int slot = decltype(slotc)::value;
+  // wave w loads rows 16 w .. 16 w + 15 of the tile, through a buffer window
+  // over its valid rows (rows past the sequence's end read as zero)
+  float sc_next = 0.f;                 // E4M3: row scale of row tid / 4 of the next tile
+  auto issue_tile = [&](int it) {
+    const int b = it / n_tt, t0 = (it % n_tt) * X_T;
+    const int valid = __builtin_amdgcn_readfirstlane(min(max(meta_len - t0, 0), X_T));
+    int64_t r0 = 0;
+    if (valid > 0) {
+      if (p.block_table != nullptr) r0 = (int64_t)__builtin_amdgcn_readfirstlane(meta_blk) * X_T;
+      else r0 = (int64_t)b * p.T_stride + t0;
+    }
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.rows + r0 * ROW_BYTES), (short)0,
+                                                        valid * ROW_BYTES, 0x00020000);
+    if constexpr (FP8) {
+      // two 512-code rows per load, plain order, into code buffer it & 1
+      char* dst = smem + X_TILE + (it & 1) * X_CODES + wave * 16 * D_C;
+      static_for<0, 8>([&](auto qc) {
+        constexpr int q = decltype(qc)::value;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + q * 1024), 16, half * ROW_BYTES + 16 * l32,
+                                                 (16 * wave + 2 * q) * ROW_BYTES, 0, 0);
+      });
+      const int t = tid >> 2;
+      sc_next = t < valid ? p.row_scale[r0 + t] : 0.f;
+    } else {
+      // one 1 KB row per load: slot `lane` takes chunk lane ^ (row & 15)
+      char* dst = smem + (it & 1) * X_TILE + wave * 16 * 1024;
+      static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + r * 1024), 16, 16 * (lane ^ r),
+                                                 (16 * wave + r) * ROW_BYTES, 0, 0);
+      });
+    }
+    if (it + 1 < n_tiles) load_meta(it + 1);
+  };
+  // E4M3: thread tid converts row tid / 4, codes 128 (tid % 4) .. + 127
+  auto convert_tile = [&](int it, float sc) {
+    const int t = tid >> 2, qd = tid & 3;
+    const char* src = smem + X_TILE + (it & 1) * X_CODES + t * D_C;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int m = 8 * qd + i;                   // 16-code chunk of the row
+      i16x8 lo, hi;
+      dequant16(*(const u32x4*)(src + 16 * m), sc, lo, hi);
+      *(i16x8*)(smem + t * 1024 + 16 * ((2 * m) ^ (t & 15))) = lo;
+      *(i16x8*)(smem + t * 1024 + 16 * ((2 * m + 1) ^ (t & 15))) = hi;
+    }
+  };
+  // staged outputs of tile `it` -> K_nope or V: thread tid stores rows
+  // 16 i + tid / 16, 16-byte chunk tid % 16
+  // (the LDS reads are inline asm: the compiler would otherwise wait for the
+  // tile loads just issued before reading LDS)
+  auto store_tile = [&](int it) {
+    const int b = it / n_tt, t0 = (it % n_tt) * X_T;
+    uint16_t* dst = (part ? p.v : p.k_nope) + ((int64_t)b * p.T_pad + t0) * p.kv_ld + h * D_NOPE;
+    const int cc = tid & 15, tr = tid >> 4;
+    const uint32_t st = stage_a + (it & 1) * X_STAGE + tr * 256 + 16 * (cc ^ tr);
+    i16x8 v[4];
+    static_for<0, 4>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      lds_read_b128<16 * i * 256>(v[i], st);     // row 16 i + tr: (t & 15) = tr
+    });
+    wait_lgkm<0>(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(i16x8*)(dst + (int64_t)(16 * i + tr) * p.kv_ld + 8 * cc) = v[i];
+  };
+  // fragment read offsets: row l32 (+ 32 tb), logical chunk 2 ks + half at
+  // slot (2 ks + half) ^ (l32 & 15); for ks = 8 m + j that is 16 m + ((2 j +
+  // half) ^ (l32 & 15)), so 8 lane offsets and an immediate cover all reads
+  uint32_t boff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) boff[j] = l32 * 1024 + 16 * ((2 * j + half) ^ (l32 & 15));
+
+  load_meta(0);
+  issue_tile(0);
+  // A fragments: weight row 32 wave + l32, columns 16 ks + 8 half .. + 7,
+  // fetched while the first tile loads; both are complete before the loop
+  // (so the compiler's own waits inside it have nothing left to wait for)
+  i16x8 aw[D_C / 16];
+  {
+    const uint16_t* W = (part ? p.w_uvt : p.w_uk) + ((int64_t)h * D_NOPE + 32 * wave + l32) * D_C + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D_C / 16; ++ks) aw[ks] = ld16(W + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < D_C / 16; ++ks) touch_reg(aw[ks]);
+  }
+  f32x16 acc[2] = {f32x16{}, f32x16{}};
+  for (int it = 0; it < n_tiles; ++it) {
+    barrier_tile_ready();       // tile it landed; every wave is past tile it - 1's products
+    uint32_t tb_a;
+    if constexpr (FP8) {
+      convert_tile(it, sc_next);
+      barrier_lds();
+      tb_a = smem_a;
+    } else {
+      tb_a = smem_a + (it & 1) * X_TILE;
+    }
+    if (it + 1 < n_tiles) issue_tile(it + 1);
+    if (it > 0) store_tile(it - 1);
+
+    i16x8 rb[X_RING][2];
+    uint32_t ba[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ba[j] = tb_a + boff[j];
+    auto issue_b = [&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      lds_read_b128<256 * (ks >> 3)>(rb[ks % X_RING][0], ba[ks & 7]);
+      lds_read_b128<256 * (ks >> 3) + 32 * 1024>(rb[ks % X_RING][1], ba[ks & 7]);
+    };
+    static_for<0, X_RING - 1>(issue_b);
+    static_for<0, D_C / 16>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      constexpr int last = D_C / 16 - 1;
+      constexpr int ahead = (last - ks) < (X_RING - 1) ? (last - ks) : (X_RING - 1);
+      if constexpr (ks + X_RING - 1 <= last) issue_b(std::integral_constant<int, ks + X_RING - 1>{});
+      constexpr int slot = ks % X_RING;
+      wait_lgkm<2 * ahead>(rb[slot][0], rb[slot][1]);
+      const bf16x8 a = __builtin_bit_cast(bf16x8, aw[ks]);
+      acc[0] = mfma32(a, __builtin_bit_cast(bf16x8, rb[slot][0]), acc[0]);
+      acc[1] = mfma32(a, __builtin_bit_cast(bf16x8, rb[slot][1]), acc[1]);
+    });
+
+    // lane holds D[n = 32 wave + 8 g + 4 half + e][t = 32 tb + l32]: staged as
+    // row t, logical chunk 4 wave + g (bytes 8 half ..) at slot chunk ^ (t & 15)
+    const uint32_t st_a = stage_a + (it & 1) * X_STAGE;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const char* src = frag_src(s, tb, csc[slot][tb]);
-      if constexpr (FP8) {
-        const u32x4 a = *(const u32x4*)src, c = *(const u32x4*)(src + 16);
+      const int t = 32 * tb + l32;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          c8[slot][tb][q] = a[q];
-          c8[slot][tb][4 + q] = c[q];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cf[slot][tb][j] = *(const i16x8*)(src + 16 * j);
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = {acc[tb][4 * g], acc[tb][4 * g + 1], acc[tb][4 * g + 2], acc[tb][4 * g + 3]};
+        lds_write_b64<0>(st_a + t * 256 + 16 * ((4 * wave + g) ^ (t & 15)) + 8 * half, pack_bf16x4(v4));
       }
+      acc[tb] = f32x16{};
     }
-  };
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();                                     // the weights are in LDS
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16{};
-  // the step loop is unrolled by the ring size so every ring slot is a
-  // compile-time index
-  static_for<0, E_AHEAD>([&](auto sc) {
-    if (decltype(sc)::value < n_steps) issue(decltype(sc)::value, sc);
-  });
-  for (int s0 = 0; s0 < n_steps; s0 += E_AHEAD + 1) {
-    static_for<0, E_AHEAD + 1>([&](auto uc) {
-      constexpr int u = decltype(uc)::value;
-      const int s = s0 + u;
-      if (s >= n_steps) return;
-      if (s + E_AHEAD < n_steps) issue(s + E_AHEAD, std::integral_constant<int, (u + E_AHEAD) % (E_AHEAD + 1)>{});
-      const int tile = s / E_NCH, ch = s % E_NCH;
-      i16x8 bf[2][4];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        if constexpr (FP8) {
-          dequant16(u32x4{c8[u][tb][0], c8[u][tb][1], c8[u][tb][2], c8[u][tb][3]}, csc[u][tb], bf[tb][0], bf[tb][1]);
-          dequant16(u32x4{c8[u][tb][4], c8[u][tb][5], c8[u][tb][6], c8[u][tb][7]}, csc[u][tb], bf[tb][2], bf[tb][3]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bf[tb][j] = cf[u][tb][j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        i16x8 af[2];
-        const uint32_t a = wo[j] + ch * 128;
-        lds_read_b128<0>(af[0], a);
-        lds_read_b128<32 * 1024>(af[1], a);
-        wait_lgkm<0>(af[0], af[1]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            acc[nb][tb] = mfma32(__builtin_bit_cast(bf16x8, af[nb]), __builtin_bit_cast(bf16x8, bf[tb][j]), acc[nb][tb]);
-      }
-      if (ch == E_NCH - 1) {
-        // lane holds D[n = 64 nq + 32 nb + 8 g + 4 half + e][t = 64 tq + 32 tb + l32]
-        const int b = tile / n_tt, t0 = (tile % n_tt) * ET;
-        const int T = p.seqlens[b];
-        uint16_t* dst = (part ? p.v : p.k_nope) + ((int64_t)b * p.T_pad + t0) * p.kv_ld + h * D_NOPE;
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int t = 64 * tq + 32 * tb + l32;
-          const bool live = t0 + t < T;
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              uint64_t v = 0;
-              if (live) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v |= (uint64_t)bf16_bits(to_bf16(acc[nb][tb][4 * g + e])) << (16 * e);
-              }
-              *(uint64_t*)(dst + (int64_t)t * p.kv_ld + 64 * nq + 32 * nb + 8 * g + 4 * half) = v;
-            }
-            acc[nb][tb] = f32x16{};
-          }
-        }
-      }
-    });
   }
+  barrier_tile_ready();
+  store_tile(n_tiles - 1);
 }
 
 // the rope keys of every row: [B, T_pad, 64] bf16 (zeros past a sequence's end)
