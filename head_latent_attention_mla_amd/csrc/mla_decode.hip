@@ -118,6 +118,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   int b, j, parts;
   int sl;
   int g;
+  int T;                                   // rows of sequence b (selected rows when SPARSE)
   auto seq_len = [&](int bb) -> int {
     if constexpr (SPARSE) return min(max(p.seqlens[bb], 0), p.k_max);
     return p.seqlens[bb];
@@ -145,18 +146,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       found[2] = all;
       return v + before;
     };
+    // the first length of the chunk (the whole chunk while B <= 256) is
+    // fetched once and kept
+    const int len_c0 = c0 < c1 ? seq_len(c0) : 0;
+    auto len_at = [&](int bb) -> int { return bb == c0 ? len_c0 : seq_len(bb); };
     int64_t tiles_mine = 0;
-    for (int bb = c0; bb < c1; ++bb) tiles_mine += (seq_len(bb) + KT - 1) / KT;
+    for (int bb = c0; bb < c1; ++bb) tiles_mine += (len_at(bb) + KT - 1) / KT;
     (void)inclusive_scan(tiles_mine);
     const int64_t total = uniform64(found[2]);
     // in [1, max(n_t, 1)]: every part holds a tile, and a sequence without
     // rows still gets one (empty) part, whose partial merges to zero
-    auto parts_of = [&](int bb) -> int {
-      const int64_t nt = (seq_len(bb) + KT - 1) / KT;
+    auto parts_from_len = [&](int len) -> int {
+      const int64_t nt = (len + KT - 1) / KT;
       if (total == 0 || nt == 0) return 1;
       const int64_t q = floor_div(nt * p.n_ranges, total);
       return (int)(q < 1 ? 1 : (q > nt ? nt : q));
     };
+    const int parts_c0 = parts_from_len(len_c0);
+    auto parts_of = [&](int bb) -> int { return bb == c0 ? parts_c0 : parts_from_len(seq_len(bb)); };
     int64_t parts_mine = 0;
     for (int bb = c0; bb < c1; ++bb) parts_mine += parts_of(bb);
     const int64_t pincl = inclusive_scan(parts_mine);
@@ -176,12 +183,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       }
       found[0] = bb;
       found[1] = q;
+      found[3] = parts_of(bb);
+      found[4] = len_at(bb);
     }
     __syncthreads();
     b = __builtin_amdgcn_readfirstlane((int)found[0]);
     const int q0 = __builtin_amdgcn_readfirstlane((int)found[1]);
+    parts = __builtin_amdgcn_readfirstlane((int)found[3]);
+    T = __builtin_amdgcn_readfirstlane((int)found[4]);
     __syncthreads();                       // the buffer is reused below
-    parts = parts_of(b);
     j = sl - q0;
     if (g == 0 && tid == 0 && j == 0) {    // where sequence b's partials are
       p.seg_first[b] = q0;
@@ -219,8 +229,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     __syncthreads();                         // the buffer is reused below
     if (flagged == 0) return;                // uniform per work-group
   }
-  const int nt_b = (seq_len(b) + KT - 1) / KT;
-  const int T = seq_len(b);
+  const int nt_b = (T + KT - 1) / KT;
   const int t_begin = (int)floor_div((int64_t)j * nt_b, parts) * KT;
   const int t_end = min(T, (int)floor_div((int64_t)(j + 1) * nt_b, parts) * KT);
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + KT - 1) / KT : 0;
@@ -233,15 +242,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   const int visible = p.causal ? (T - p.s_q + jq + 1) : T;
   const int lim = min(visible, t_end);
 
+  // the latent queries of the owned rows, B fragments of the 36 k-steps
+  // (nothing waits for them before the first tile's barrier, so they load
+  // together with the first tile).  Rows past the last query row take row
+  // 0's query: their scores are computed but never stored.
   bf16x8 qf[ROWW / 16];
   {
     const uint16_t* qrow = p.q_lat + ((int64_t)b * p.R + (own_ok ? own_r : 0)) * ROWW + half * 8;
 #pragma unroll
-    for (int ks = 0; ks < ROWW / 16; ++ks) {
-      i16x8 v = *(const i16x8*)(qrow + ks * 16);
-      if (!own_ok) v = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < ROWW / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const i16x8*)(qrow + ks * 16));
   }
 
   // ---- tile loader.  Wave w copies rows 16w..16w+15 of the tile: 18 loads
@@ -265,7 +274,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   // per-tile load state: buffer window over the tile's rows
   auto tile_base = [&](int tile) -> int64_t {  // element index of the tile's first row
     const int ts = t_begin + tile * KT;
-    if (PAGED) return (int64_t)p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)] * KT;
+    // (the table entry moved to a scalar register: a buffer resource must be uniform)
+    if (PAGED) return (int64_t)__builtin_amdgcn_readfirstlane(p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)]) * KT;
     return (int64_t)b * p.T_stride + ts;
   };
   // live = false gives an empty window: its loads fetch nothing and write zeros
@@ -453,7 +463,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       for (int i = 0; i < 4; ++i) qa[i] = tb_a + qoff[i];
       // k-steps of A fragments in flight (the sparse variant gives one up for
       // the prefetched positions)
-      constexpr int QK_AHEAD = SPARSE ? 2 : 3;
+      constexpr int QK_AHEAD = (SPARSE || FP8) ? 2 : 3;
       i16x8 ra[QK_AHEAD + 1][2];
       auto issue_qk = [&](auto ksc) {
         constexpr int ks = decltype(ksc)::value;
