@@ -282,11 +282,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
   auto tile_rsrc = [&](int tile, bool live) {
     if constexpr (SPARSE) {
       // the whole sequence: a selected position outside it reads as a zero row
+      const int src_rows = __builtin_amdgcn_readfirstlane(live ? p.src_len[b] : 0);   // uniform
       return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + (int64_t)b * p.T_stride * ROWW * ELEM), (short)0,
-                                               live ? p.src_len[b] * ROWW * ELEM : 0, 0x00020000);
+                                               src_rows * ROWW * ELEM, 0x00020000);
     }
     const int ts = t_begin + tile * KT;
-    const int valid = live ? min(KT, T - ts) : 0;
+    const int valid = __builtin_amdgcn_readfirstlane(live ? min(KT, T - ts) : 0);   // uniform
     return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW * ELEM), (short)0,
                                              valid * ROWW * ELEM, 0x00020000);
   };

@@ -106,9 +106,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
   int b, j, parts, sl, g;
   if (!plan_work(p, (int64_t*)pbuf, b, j, parts, sl, g)) return;   // surplus work-group
   const int nt_b = (p.seqlens[b] + KT - 1) / KT;
-  const int T = p.seqlens[b];
-  const int t_begin = (int)floor_div((int64_t)j * nt_b, parts) * KT;
-  const int t_end = min(T, (int)floor_div((int64_t)(j + 1) * nt_b, parts) * KT);
+  // (all uniform: kept in scalar registers, as the tile loads' buffer
+  // windows must be)
+  const int T = __builtin_amdgcn_readfirstlane(p.seqlens[b]);
+  const int t_begin = __builtin_amdgcn_readfirstlane((int)floor_div((int64_t)j * nt_b, parts) * KT);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(T, (int)floor_div((int64_t)(j + 1) * nt_b, parts) * KT));
   const int n_tiles = t_end > t_begin ? (t_end - t_begin + KT - 1) / KT : 0;
 
   // ---- own query row; its latent query quantised to E4M3 with a row scale
@@ -171,13 +173,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
   const char* rows = (const char*)p.rows;
   auto tile_base = [&](int tile) -> int64_t {   // row index of the tile's first row
     const int ts = t_begin + tile * KT;
-    if (PAGED) return (int64_t)p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)] * KT;
+    // (the table entry moved to a scalar register: a buffer resource must be uniform)
+    if (PAGED) return (int64_t)__builtin_amdgcn_readfirstlane(p.block_table[(int64_t)b * p.max_blocks + (ts >> 6)]) * KT;
     return (int64_t)b * p.T_stride + ts;
   };
   const int soff = wave * (16 * ROWW);
   auto issue_tile = [&](int tile, int buf) {
     const int ts = t_begin + tile * KT;
-    const int valid = min(KT, T - ts);
+    const int valid = __builtin_amdgcn_readfirstlane(min(KT, T - ts));
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW), (short)0,
                                                         valid * ROWW, 0x00020000);
     char* dst = smem + buf * STAGE + wave * (16 * ROWW);

@@ -358,7 +358,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
   for (int i = 0; i < 2; ++i) offr[i] = (uint32_t)((lane >> 3) * 128 + 16 * ((lane & 7) ^ (4 * i + (lane >> 4))));
   auto issue_tile = [&](int tile, int buf) {
     const int64_t r0 = (int64_t)tile * KT;
-    const int valid = max(0, min(KT, T_u - (int)r0));
+    // (in a scalar register: a buffer resource must be uniform)
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(KT, T_u - (int)r0)));
     const int kv_bytes = valid * (int)RS;
     const auto kn = __builtin_amdgcn_make_buffer_rsrc((void*)(kn_base + r0 * RS), (short)0, kv_bytes, 0x00020000);
     const auto vv = __builtin_amdgcn_make_buffer_rsrc((void*)(v_base + r0 * RS), (short)0, kv_bytes, 0x00020000);
