@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 # the split-T kernel's sources: a traffic figure taken with hardware counters
 # holds only for the code it was taken on
 KERNEL_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_decode.hip",
+                  "head_latent_attention_mla_amd/csrc/mla_decode_f8.hip",
+                  "head_latent_attention_mla_amd/csrc/mla_plan.h",
                   "head_latent_attention_mla_amd/csrc/mla_common.h",
                   "head_latent_attention_mla_amd/csrc/mla_internal.h",
                   "head_latent_attention_mla_amd/csrc/mla_split_store.h")
@@ -593,7 +595,7 @@ def main():
         "peak": HBM_PEAK_GBS if hbm_bound else peak_mfma,
         "unit": "GB/s" if hbm_bound else "TFLOP/s",
         "frac": round((scan_gbs / HBM_PEAK_GBS) if hbm_bound else (scan_tflops / peak_mfma), 4),
-        "traffic": None if (sparse or f8m) else measured_traffic(w.name),
+        "traffic": measured_traffic(w.name + ("_fp8math" if f8m else "")),
         "algorithmic_bytes_per_launch": cnt["bytes_scan"],
         "algorithmic_flops_per_launch": cnt["flops_scan"],
         "avg_launch_us": round(kern_us[names[1]], 2),

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
                                                           const uint16_t* __restrict__ w_uv,
                                                           uint16_t* __restrict__ out, void* o_lat,
                                                           int o_bf16, float* lse_out) {
-  __shared__ __attribute__((aligned(1024))) char wt[3][CO_WBYTES];   // W_UV chunks, two loads ahead
+  __shared__ __attribute__((aligned(1024))) char wt[3][CO_WBYTES];   // W_UV chunks 0-2, then 3 in slot 0
   __shared__ __attribute__((aligned(1024))) char at[2][CO_ABYTES];   // [hi, lo]
   const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -284,8 +284,6 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
                                        (lds_void_t*)(dst + i * 256 * 16), 16, 0, 0);
     }
   };
-  issue_w(0);
-  issue_w(1);
 
   // ---- merge: thread -> row r = tid / TPR, columns VW (tid % TPR) + VW TPR i
   // (VW = 8 bf16 or 4 fp32 partial values: 16-byte loads, so the TPR threads
@@ -334,6 +332,11 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
     float l[SG];
     Raw d[SG][NCH];
     load_group(0, l, d);
+    // the first three W_UV chunks load behind the first group of partials
+    // (so the merge waits only for its own loads) and during the merge
+    issue_w(0);
+    issue_w(1);
+    issue_w(2);
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
@@ -407,14 +410,17 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
   constexpr int NKC = D_C / CO_KC;
   constexpr int W_LOADS = CO_KC * AQ_CHUNKS / 256;     // direct loads per thread per chunk
   for (int kc = 0; kc < NKC; ++kc) {
-    // this thread's loads of chunk kc are done once at most those of chunk
-    // kc + 1 are outstanding (the merge's loads were consumed before)
-    if (kc + 1 < NKC)
+    // chunk kc of this thread's loads is done once at most the younger
+    // chunks' loads are outstanding: chunks 1 and 2 at kc = 0, then one
+    // chunk (2, then 3, issued at kc = 1 into the slot chunk 0 used)
+    if (kc == 0)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * W_LOADS) : "memory");
+    else if (kc + 1 < NKC)
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_LOADS) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // chunk kc (and the merged operands) visible; chunk kc-1 consumed
-    if (kc + 2 < NKC) issue_w(kc + 2);
+    if (kc == 1) issue_w(3);
     const char* w = wt[kc % 3];
 #pragma unroll
     for (int ks = 0; ks < CO_KC / 16; ++ks) {
