@@ -471,9 +471,14 @@ mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv, cons
 }
 
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen) {
-  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || H > (1 << 16)) return 0;
-  // W_UV re-laid out per head with the latent dimension contiguous
-  return align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t));
+  if (B <= 0 || s_q <= 0 || H <= 0 || max_seqlen <= 0 || H > (1 << 16) || B > (1 << 16)) return 0;
+  if (s_q > mla::NAIVE_MAX_SQ || max_seqlen > (1 << 28)) return 0;
+  if ((double)B * s_q * H * max_seqlen * 4.0 > (double)(1ull << 46)) return 0;   // 64 TiB: not a real size
+  // W_UV re-laid out per head with the latent dimension contiguous, the
+  // scores / probabilities [B, s_q, H, T_cap] and their sums [B, s_q, H]
+  const size_t t_cap = ((size_t)max_seqlen + 63) / 64 * 64;
+  return align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t)) +
+         align_up((size_t)B * s_q * H * t_cap * sizeof(float)) + align_up((size_t)B * s_q * H * sizeof(float));
 }
 
 mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv, const void* w_uk, const void* w_uv,
@@ -496,13 +501,19 @@ mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv, const void* w_
   p.seqlens = kv->seqlens;
   p.w_uk = (const uint16_t*)w_uk;
   p.w_uv = (const uint16_t*)w_uv;
+  const size_t t_cap = ((size_t)kv->max_seqlen + 63) / 64 * 64;
+  const size_t wuvt_bytes = align_up((size_t)H * mla::D_V * mla::D_C * sizeof(uint16_t));
+  const size_t score_bytes = align_up((size_t)B * s_q * H * t_cap * sizeof(float));
   p.w_uvt = (uint16_t*)workspace;
+  p.scores = (float*)((char*)workspace + wuvt_bytes);
+  p.lsum = (float*)((char*)workspace + wuvt_bytes + score_bytes);
   p.out = (uint16_t*)out;
   p.T_stride = kv->T_stride;
   p.max_blocks = kv->max_blocks;
   p.B = B;
   p.s_q = s_q;
   p.H = H;
+  p.T_cap = (int32_t)t_cap;
   p.scale_log2 = softmax_scale * 1.4426950408889634f;
   p.causal = causal;
   p.fp8 = kv->dtype == MLA_FP8_E4M3;

@@ -64,10 +64,13 @@ struct NaiveParams {
   const uint16_t* w_uk;         // bf16 [H, 128, 512]
   const uint16_t* w_uv;         // bf16 [H, 512, 128]
   uint16_t* w_uvt;              // workspace: bf16 [H, 128, 512]
+  float* scores;                // workspace: fp32 [B, s_q, H, T_cap], scores then probabilities
+  float* lsum;                  // workspace: fp32 [B, s_q, H], sums of the probabilities
   uint16_t* out;                // bf16 [B, s_q, H, 128]
   int64_t T_stride;
   int32_t max_blocks;
   int32_t B, s_q, H;
+  int32_t T_cap;                // max_seqlen rounded up to 64 (row pitch of scores)
   float scale_log2;
   int32_t causal;
   int32_t fp8;

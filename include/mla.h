@@ -343,9 +343,12 @@ mla_status mla_sparse_decode_attn(const void* q_lat, const mla_kv_desc* kv,
  * Expanded keys and values are rounded to bf16 (as a materialised bf16 K/V
  * would be); scores, softmax and the value sum accumulate in fp32.
  * s_q must be <= 4 (else MLA_ERR_UNSUPPORTED).  softmax_scale finite and > 0.
- * workspace: ws_bytes >= mla_naive_workspace_bytes(...) (= H * 128 * 512 * 2
- * rounded up to 256, a per-head transposed copy of W_UV written by the call);
- * 0 from mla_naive_workspace_bytes means an invalid size argument. */
+ * workspace: ws_bytes >= mla_naive_workspace_bytes(...): a per-head transposed
+ * copy of W_UV (H * 128 * 512 bf16), the scores of every (query row, cached
+ * row) pair (B * s_q * H * T_cap fp32, T_cap = max_seqlen rounded up to 64)
+ * and their row sums (B * s_q * H fp32), each rounded up to 256 bytes, all
+ * written by the call; 0 from mla_naive_workspace_bytes means an invalid or
+ * unreasonably large size argument (s_q > 4 included). */
 size_t mla_naive_workspace_bytes(int32_t B, int32_t s_q, int32_t H, int32_t max_seqlen);
 mla_status mla_naive_decode(const void* q, const mla_kv_desc* kv,
                             const void* w_uk, const void* w_uv,

@@ -151,8 +151,13 @@ def _naive(m, kv, B=2, s_q=1, H=16, scale=0.07, causal=0, ws_bytes=1 << 30, q=0x
 
 def test_naive_rejects_bad_arguments(m):
     ws = m._lib.mla_naive_workspace_bytes
-    assert ws(2, 1, 16, 256) == 16 * 128 * 512 * 2
+    # transposed W_UV, scores [B, s_q, H, T_cap] fp32 and row sums [B, s_q, H] fp32, each 256-aligned
+    need = 16 * 128 * 512 * 2 + 2 * 1 * 16 * 256 * 4 + 256
+    assert ws(2, 1, 16, 256) == need
+    assert ws(2, 2, 16, 250) == 16 * 128 * 512 * 2 + 2 * 2 * 16 * 256 * 4 + 256   # T_cap = 256
     assert ws(0, 1, 16, 256) == 0 and ws(2, 1, 16, 0) == 0
+    assert ws(2, 5, 16, 256) == 0                   # at most 4 query tokens
+    assert ws(65536, 4, 65536, 1 << 28) == 0        # not a real size
     assert _naive(m, _kv(), q=None) == ARG
     assert _naive(m, _kv(), out=None) == ARG
     assert _naive(m, _kv(rows=None)) == ARG
@@ -160,7 +165,7 @@ def test_naive_rejects_bad_arguments(m):
     assert _naive(m, _kv(), scale=-1.0) == ARG
     assert _naive(m, _kv(max_seqlen=8), s_q=5) == UNSUP     # at most 4 query tokens
     assert _naive(m, _kv(block_table=0x7000, block_size=16, max_blocks=16)) == UNSUP
-    assert _naive(m, _kv(), ws_bytes=16 * 128 * 512 * 2 - 1) == WS
+    assert _naive(m, _kv(), ws_bytes=need - 1) == WS
 
 
 def test_combine_out_rejects_bad_arguments(m):

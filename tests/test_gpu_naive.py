@@ -46,7 +46,8 @@ def test_naive_vs_oracle_and_absorbed(mla, kind):
 
 
 def test_naive_workspace_and_limits(mla):
-    assert mla.naive_workspace_bytes(2, 1, 128, 256) == 128 * 128 * 512 * 2
+    # transposed W_UV + fp32 scores [2, 1, 128, 256] + row sums [2, 1, 128]
+    assert mla.naive_workspace_bytes(2, 1, 128, 256) == 128 * 128 * 512 * 2 + 2 * 128 * 256 * 4 + 1024
     assert mla.naive_workspace_bytes(0, 1, 128, 256) == 0
     w = small("verify").with_(s_q=5)
     inp = W.generate(w)
