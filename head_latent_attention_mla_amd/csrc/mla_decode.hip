@@ -354,24 +354,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     const int ts = t_begin + tile * KT;
     return (ts + cv_row < T) ? p.row_scale[tile_base(tile) + cv_row] : 0.f;
   };
+  // the nine 16-code chunks are read first (one LDS round trip, not nine),
+  // then converted two values per conversion instruction and written
   auto convert_tile = [&](int buf, float scale) {
-    const char* src = smem + TILE_BYTES + buf * STAGE_BYTES + cv_row * ROWW;
+    const char* src = smem + TILE_BYTES + buf * STAGE_BYTES + cv_row * ROWW + cv_q * 9 * 16;
+    u32x4 w[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = *(const u32x4*)(src + i * 16);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       const int m = cv_q * 9 + i;                 // 16-code chunk of the row
-      const u32x4 w = *(const u32x4*)(src + m * 16);
-      i16x8 o[2];
+      uint64_t o[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
-        o[d >> 1][4 * (d & 1) + 0] = (short)bf16_bits(to_bf16(lo[0] * scale));
-        o[d >> 1][4 * (d & 1) + 1] = (short)bf16_bits(to_bf16(lo[1] * scale));
-        o[d >> 1][4 * (d & 1) + 2] = (short)bf16_bits(to_bf16(hi[0] * scale));
-        o[d >> 1][4 * (d & 1) + 3] = (short)bf16_bits(to_bf16(hi[1] * scale));
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], true);
+        o[d] = pack_bf16x4(f32x4{lo[0] * scale, lo[1] * scale, hi[0] * scale, hi[1] * scale});
       }
-      *(i16x8*)(smem + lds_off(cv_row, 16 * m)) = o[0];
-      *(i16x8*)(smem + lds_off(cv_row, 16 * m + 8)) = o[1];
+      *(u32x4*)(smem + lds_off(cv_row, 16 * m)) = u32x4{(uint32_t)o[0], (uint32_t)(o[0] >> 32), (uint32_t)o[1], (uint32_t)(o[1] >> 32)};
+      *(u32x4*)(smem + lds_off(cv_row, 16 * m + 8)) = u32x4{(uint32_t)o[2], (uint32_t)(o[2] >> 32), (uint32_t)o[3], (uint32_t)(o[3] >> 32)};
     }
   };
 
