@@ -130,28 +130,30 @@ __global__ __launch_bounds__(256, 1) void naive_pass_kernel(NaiveParams p, int n
       });
     }
   };
-  // E4M3: thread tid converts row tid / 4, quarter tid % 4 (144 codes)
+  // E4M3: thread tid converts row tid / 4, quarter tid % 4 (144 codes); the
+  // nine 16-code chunks are read first, then converted two values per
+  // conversion instruction
   auto convert_tile = [&](int buf, float scale) {
     const int t = tid >> 2, cq = tid & 3;
-    const char* src = smem + XTILE + buf * XSTAGE + t * ROWW;
+    const char* src = smem + XTILE + buf * XSTAGE + t * ROWW + cq * 9 * 16;
+    u32x4 w[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) w[i] = *(const u32x4*)(src + i * 16);
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       const int m = cq * 9 + i;
-      const u32x4 w = *(const u32x4*)(src + m * 16);
-      i16x8 o[2];
+      uint64_t o[4];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
-        o[d >> 1][4 * (d & 1) + 0] = (short)bf16_bits(to_bf16(lo[0] * scale));
-        o[d >> 1][4 * (d & 1) + 1] = (short)bf16_bits(to_bf16(lo[1] * scale));
-        o[d >> 1][4 * (d & 1) + 2] = (short)bf16_bits(to_bf16(hi[0] * scale));
-        o[d >> 1][4 * (d & 1) + 3] = (short)bf16_bits(to_bf16(hi[1] * scale));
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], true);
+        o[d] = pack_bf16x4(f32x4{lo[0] * scale, lo[1] * scale, hi[0] * scale, hi[1] * scale});
       }
-      *(i16x8*)(smem + xoff(t, 16 * m)) = o[0];
-      *(i16x8*)(smem + xoff(t, 16 * m + 8)) = o[1];
+      *(u32x4*)(smem + xoff(t, 16 * m)) = u32x4{(uint32_t)o[0], (uint32_t)(o[0] >> 32), (uint32_t)o[1], (uint32_t)(o[1] >> 32)};
+      *(u32x4*)(smem + xoff(t, 16 * m + 8)) = u32x4{(uint32_t)o[2], (uint32_t)(o[2] >> 32), (uint32_t)o[3], (uint32_t)(o[3] >> 32)};
     }
   };
+
   // B-fragment reads: tile row l32 (+ 32), logical chunk 2 ks + half; for
   // ks = 4 m + i the XOR touches only the low 3 bits, so 4 lane offsets and
   // an immediate 128 m cover every read (rows 32 apart share the pattern)

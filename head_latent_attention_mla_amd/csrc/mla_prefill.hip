@@ -48,18 +48,17 @@ __device__ __forceinline__ int64_t cache_row(const PrefillParams& p, int b, int 
 }
 
 // 16 consecutive e4m3 codes times the row scale -> two bf16x8 fragments
+// (two values per conversion instruction)
 __device__ __forceinline__ void dequant16(u32x4 w, float s, i16x8& lo, i16x8& hi) {
+  uint64_t o[4];
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], false);
     const auto c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[d], true);
-    i16x8& o = d < 2 ? lo : hi;
-    const int e = 4 * (d & 1);
-    o[e + 0] = (short)bf16_bits(to_bf16(a[0] * s));
-    o[e + 1] = (short)bf16_bits(to_bf16(a[1] * s));
-    o[e + 2] = (short)bf16_bits(to_bf16(c[0] * s));
-    o[e + 3] = (short)bf16_bits(to_bf16(c[1] * s));
+    o[d] = pack_bf16x4(f32x4{a[0] * s, a[1] * s, c[0] * s, c[1] * s});
   }
+  lo = __builtin_bit_cast(i16x8, u32x4{(uint32_t)o[0], (uint32_t)(o[0] >> 32), (uint32_t)o[1], (uint32_t)(o[1] >> 32)});
+  hi = __builtin_bit_cast(i16x8, u32x4{(uint32_t)o[2], (uint32_t)(o[2] >> 32), (uint32_t)o[3], (uint32_t)(o[3] >> 32)});
 }
 
 // ---------------------------------------------------------------------------
