@@ -238,52 +238,115 @@ __global__ __launch_bounds__(256) void absorb_out_kernel(const void* __restrict_
 // ---------------------------------------------------------------------------
 // combine_out: the log-sum-exp merge of the split partials fused with the
 // projection through W_UV, so the latent output never round-trips through
-// HBM.  grid (H, ceil(N / 32)), 4 waves.  Per work-group: merge the partials
-// of 32 query rows of one head (the merge arithmetic is the one of the
-// stand-alone merge kernel, term for term), stage them as bf16 high + low
-// MFMA operands in LDS, then stream W_UV[h] through LDS in four 128-row
-// chunks; wave w computes output columns 32 w .. 32 w + 31.
+// HBM.  grid (H, ceil(N / 32)), 4 waves; a work-group takes 32 query rows of
+// one head, and wave w computes output columns 32 w .. 32 w + 31.  The merge
+// arithmetic is the one of the stand-alone merge kernel, term for term (splits
+// added in order, the same weights), and the projection accumulates in the
+// order of absorb_out, so the bits are the same as the two steps apart.
+//
+// Two paths, chosen per work-group from the split counts of its rows:
+//  * at most four splits per row (the common case): the partials (registers)
+//    and W_UV rows (LDS, all of W_UV[h] resident) of the four 128-column
+//    chunks are issued chunk by chunk at the start; each chunk is merged,
+//    staged as bf16 high (+ low) MFMA operands and projected as soon as its
+//    loads are in, so the merge and the projection of one chunk overlap the
+//    arrival of the next;
+//  * more splits: all 512 columns of a row are merged four splits at a time,
+//    then projected through W_UV in four staged chunks.
 // ---------------------------------------------------------------------------
 constexpr int CO_ROWS = 32;
-constexpr int CO_KC = 128;                        // W_UV rows per staged chunk
-constexpr int CO_WBYTES = CO_KC * D_V * 2;        // 32 KB
-constexpr int CO_ABYTES = CO_ROWS * D_C * 2;      // one bf16 operand plane, 32 KB
+constexpr int CO_KC = 128;                        // W_UV rows (latent columns) per chunk
+constexpr int CO_NKC = D_C / CO_KC;               // 4 chunks
+constexpr int CO_WBYTES = CO_KC * D_V * 2;        // 32 KB: W_UV rows of one chunk
+constexpr int CO_W_LOADS = CO_WBYTES / (256 * 16);   // 8 direct loads per thread per chunk
+constexpr int CO_SG = 4;                          // splits per load group
+constexpr int CO_LDS = 160 * 1024;
+// many-split path: [32][512] bf16 operand planes
+constexpr int CO_ABYTES = CO_ROWS * D_C * 2;      // 32 KB
+static_assert(3 * CO_WBYTES + 2 * CO_ABYTES <= CO_LDS, "LDS budget (many splits)");
+// four-split path: [32][128] bf16 operand planes of one chunk, high and low,
+// double-buffered over the chunks
+constexpr int CF_ABYTES = CO_ROWS * CO_KC * 2;    // 8 KB
+static_assert(CO_NKC * CO_WBYTES + 4 * CF_ABYTES <= CO_LDS, "LDS budget (four splits)");
 
 // row-major [32][512] bf16 operand plane; the 16-byte chunk index is XORed
 // with the row so that the 32 rows of an MFMA fragment read hit all banks
 __device__ __forceinline__ int co_aoff(int r, int k) {
   return r * (D_C * 2) + (((k >> 3) ^ (r & 15)) << 4) + (k & 7) * 2;
 }
+// [32][128] bf16 plane of one chunk: 16-byte chunk c16 of row r, XORed the same way
+__device__ __forceinline__ uint32_t cf_aoff(int r, int c16) {
+  return (uint32_t)(r * (CO_KC * 2) + ((c16 ^ (r & 15)) << 4));
+}
 
+// W_UV rows kc*128 .. +127 of one head into a 32 KB LDS slot (direct loads,
+// chunk index XORed as aq_off expects)
+__device__ __forceinline__ void co_issue_w(const uint16_t* wsrc, char* slot, int kc, int wave, int lane) {
+  char* dst = slot + wave * 64 * 16;
+#pragma unroll
+  for (int i = 0; i < CO_W_LOADS; ++i) {
+    const int s = i * 256 + wave * 64 + lane;
+    const int k = s / AQ_CHUNKS;
+    const int cc = (s % AQ_CHUNKS) ^ chunk_swz(k);
+    __builtin_amdgcn_global_load_lds((const void*)(wsrc + (int64_t)(kc * CO_KC + k) * D_V + cc * 8),
+                                     (lds_void_t*)(dst + i * 256 * 16), 16, 0, 0);
+  }
+}
+
+// Global loads issued as inline asm, in program order among the direct
+// W_UV loads, so that explicit vmcnt waits can count them (the compiler's
+// own waits turn into vmcnt(0) while direct-to-LDS loads are in flight).  A
+// consumer first calls wait_vm<N>() on the loaded registers: N = loads issued
+// after the one waited for.
+__device__ __forceinline__ void gload_b128(u32x4& d, const void* p) {
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(d) : "v"(p) : "memory");
+}
+__device__ __forceinline__ void gload_b32(float& d, const void* p) {
+  asm volatile("global_load_dword %0, %1, off" : "=v"(d) : "v"(p) : "memory");
+}
+template <int N, typename... R>
+__device__ __forceinline__ void wait_vm(R&... regs) {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+  (touch_reg(regs), ...);
+}
+
+// the 32 x 128 output block of the work-group: staged in LDS (wave w wrote
+// its columns), then written as whole 256-byte rows
+__device__ __forceinline__ void co_store_out(const f32x16& acc, char* stage, uint16_t* out, int n0, int N, int H,
+                                             int h, int tid, int wave, int half, int l32) {
+  uint16_t(*ot)[D_V + 8] = (uint16_t(*)[D_V + 8])stage;
+  const int v0 = wave * 32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ot[8 * (r >> 2) + 4 * half + (r & 3)][v0 + l32] = bf16_bits(to_bf16(acc[r]));
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int chunk = i * 256 + tid;   // 32 rows x 16 chunks of 16 B
+    const int rr = chunk >> 4, cc = chunk & 15;
+    const int n = n0 + rr;
+    if (n < N) *(i16x8*)(out + ((int64_t)n * H + h) * D_V + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+  }
+}
+
+// Many splits per row: merge all 512 columns (four splits at a time), stage
+// them as bf16 high + low operands in LDS, then stream W_UV[h] through LDS in
+// four 128-row chunks.
 template <bool PB16>
-__global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict__ part_o,
-                                                          const float* __restrict__ part_lse,
-                                                          const int32_t* __restrict__ seg_first,
-                                                          const int32_t* __restrict__ seg_count,
-                                                          int s_q, int H, int N,
-                                                          const uint16_t* __restrict__ w_uv,
-                                                          uint16_t* __restrict__ out, void* o_lat,
-                                                          int o_bf16, float* lse_out) {
-  __shared__ __attribute__((aligned(1024))) char wt[3][CO_WBYTES];   // W_UV chunks 0-2, then 3 in slot 0
-  __shared__ __attribute__((aligned(1024))) char at[2][CO_ABYTES];   // [hi, lo]
+__device__ __forceinline__ void combine_out_many(char* smem, const void* __restrict__ part_o,
+                                                 const float* __restrict__ part_lse,
+                                                 const int32_t* __restrict__ seg_first,
+                                                 const int32_t* __restrict__ seg_count, int s_q, int H, int N,
+                                                 const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ out,
+                                                 void* o_lat, int o_bf16, float* lse_out) {
+  char* const wt = smem;                              // [3][CO_WBYTES]: W_UV chunks 0-2, then 3 in slot 0
+  char* const at = smem + 3 * CO_WBYTES;              // [2][CO_ABYTES]: [hi, lo]
   const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int R = s_q * H;
   const uint16_t* wsrc = w_uv + (int64_t)h * D_C * D_V;
-
-  auto issue_w = [&](int kc) {
-    char* dst = wt[kc % 3] + wave * 64 * 16;
-#pragma unroll
-    for (int i = 0; i < CO_KC * AQ_CHUNKS / 256; ++i) {
-      const int slot = i * 256 + wave * 64 + lane;
-      const int k = slot / AQ_CHUNKS;
-      const int cc = (slot % AQ_CHUNKS) ^ chunk_swz(k);
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc + (int64_t)(kc * CO_KC + k) * D_V + cc * 8),
-                                       (lds_void_t*)(dst + i * 256 * 16), 16, 0, 0);
-    }
-  };
 
   // ---- merge: thread -> row r = tid / TPR, columns VW (tid % TPR) + VW TPR i
   // (VW = 8 bf16 or 4 fp32 partial values: 16-byte loads, so the TPR threads
@@ -305,10 +368,9 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
     // together (indices past the last split reload it and get weight 0), and
     // added in split order.  The first group's partials are loaded with the
     // log-sum-exps, before the maximum is known (it only sets their weights).
-    constexpr int SG = 4;
-    auto load_group = [&](int s0, float (&l)[SG], Raw (&d)[SG][NCH]) {
+    auto load_group = [&](int s0, float (&l)[CO_SG], Raw (&d)[CO_SG][NCH]) {
 #pragma unroll
-      for (int u = 0; u < SG; ++u) {
+      for (int u = 0; u < CO_SG; ++u) {
         const int s = max(min(s0 + u, n_split - 1), 0);
         l[u] = part_lse[(sb + s) * R + row];
         const int64_t src = ((sb + s) * R + row) * D_C + cq;
@@ -329,20 +391,20 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
         return x;
       }
     };
-    float l[SG];
-    Raw d[SG][NCH];
+    float l[CO_SG];
+    Raw d[CO_SG][NCH];
     load_group(0, l, d);
     // the first three W_UV chunks load behind the first group of partials
     // (so the merge waits only for its own loads) and during the merge
-    issue_w(0);
-    issue_w(1);
-    issue_w(2);
+    co_issue_w(wsrc, wt, 0, wave, lane);
+    co_issue_w(wsrc, wt + CO_WBYTES, 1, wave, lane);
+    co_issue_w(wsrc, wt + 2 * CO_WBYTES, 2, wave, lane);
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < SG; ++u) mx = fmaxf(mx, l[u]);
-    for (int s0 = SG; s0 < n_split; s0 += SG) {
+    for (int u = 0; u < CO_SG; ++u) mx = fmaxf(mx, l[u]);
+    for (int s0 = CO_SG; s0 < n_split; s0 += CO_SG) {
 #pragma unroll
-      for (int u = 0; u < SG; ++u) mx = fmaxf(mx, part_lse[(sb + min(s0 + u, n_split - 1)) * R + row]);
+      for (int u = 0; u < CO_SG; ++u) mx = fmaxf(mx, part_lse[(sb + min(s0 + u, n_split - 1)) * R + row]);
     }
     float wsum = 0.f;
     f32x4 acc[NCH][VW / 4];
@@ -350,13 +412,13 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
       for (int j = 0; j < VW / 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_split; s0 += SG) {
+    for (int s0 = 0; s0 < n_split; s0 += CO_SG) {
       if (s0 > 0) load_group(s0, l, d);
-      float w[SG];
+      float w[CO_SG];
 #pragma unroll
-      for (int u = 0; u < SG; ++u) w[u] = (s0 + u < n_split && l[u] != -INFINITY) ? exp2f(l[u] - mx) : 0.f;
+      for (int u = 0; u < CO_SG; ++u) w[u] = (s0 + u < n_split && l[u] != -INFINITY) ? exp2f(l[u] - mx) : 0.f;
 #pragma unroll
-      for (int u = 0; u < SG; ++u) {
+      for (int u = 0; u < CO_SG; ++u) {
         if (w[u] == 0.f) continue;      // absent or empty split: its partial may hold anything
         wsum += w[u];
 #pragma unroll
@@ -389,8 +451,8 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
         }
         const uint64_t ph = (uint64_t)hi[0] | ((uint64_t)hi[1] << 16) | ((uint64_t)hi[2] << 32) | ((uint64_t)hi[3] << 48);
         const uint64_t pl = (uint64_t)lo[0] | ((uint64_t)lo[1] << 16) | ((uint64_t)lo[2] << 32) | ((uint64_t)lo[3] << 48);
-        *(uint64_t*)(at[0] + co_aoff(r, k)) = ph;
-        *(uint64_t*)(at[1] + co_aoff(r, k)) = pl;
+        *(uint64_t*)(at + co_aoff(r, k)) = ph;
+        *(uint64_t*)(at + CO_ABYTES + co_aoff(r, k)) = pl;
       }
     if (ok && lse_out != nullptr && (tid % TPR) == 0)
       lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
@@ -407,45 +469,274 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* __restrict
   const int grp = (lane >> 4) & 1, jj = lane & 15;
   const int bcol = v0 + grp * 16 + 4 * (jj & 3);
   f32x16 acc = f32x16{};
-  constexpr int NKC = D_C / CO_KC;
-  constexpr int W_LOADS = CO_KC * AQ_CHUNKS / 256;     // direct loads per thread per chunk
-  for (int kc = 0; kc < NKC; ++kc) {
+  for (int kc = 0; kc < CO_NKC; ++kc) {
     // chunk kc of this thread's loads is done once at most the younger
     // chunks' loads are outstanding: chunks 1 and 2 at kc = 0, then one
     // chunk (2, then 3, issued at kc = 1 into the slot chunk 0 used)
     if (kc == 0)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * W_LOADS) : "memory");
-    else if (kc + 1 < NKC)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(W_LOADS) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CO_W_LOADS) : "memory");
+    else if (kc + 1 < CO_NKC)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CO_W_LOADS) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // chunk kc (and the merged operands) visible; chunk kc-1 consumed
-    if (kc == 1) issue_w(3);
-    const char* w = wt[kc % 3];
+    if (kc == 1) co_issue_w(wsrc, wt, 3, wave, lane);
+    const char* w = wt + (kc % 3) * CO_WBYTES;
 #pragma unroll
     for (int ks = 0; ks < CO_KC / 16; ++ks) {
       const int kg = kc * CO_KC + ks * 16 + half * 8;        // A columns of this lane
-      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *(const i16x8*)(at[0] + co_aoff(l32, kg)));
-      const bf16x8 alo = __builtin_bit_cast(bf16x8, *(const i16x8*)(at[1] + co_aoff(l32, kg)));
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *(const i16x8*)(at + co_aoff(l32, kg)));
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, *(const i16x8*)(at + CO_ABYTES + co_aoff(l32, kg)));
       const int krow = ks * 16 + 8 * half + (jj >> 2);
       const bf16x8 bw = join_tr(ds_read_tr16(w + aq_off(krow, bcol)), ds_read_tr16(w + aq_off(krow + 4, bcol)));
       acc = mfma32(ahi, bw, acc);
       if (!o_bf16) acc = mfma32(alo, bw, acc);
     }
   }
-  // ---- stage the 32 x 128 output block, then write whole 256-byte rows
   __syncthreads();
-  uint16_t(*ot)[D_V + 8] = (uint16_t(*)[D_V + 8])at[0];
+  co_store_out(acc, at, out, n0, N, H, h, tid, wave, half, l32);
+}
+
+// At most four splits per row: W_UV[h] resident in LDS, the partials of the
+// four 128-column chunks streaming behind it (see above).  Thread -> row
+// r = tid / 8 and, per chunk, 16 columns: bf16 partials in two 16-byte loads
+// (columns 8 (tid % 8) and 64 + 8 (tid % 8)), fp32 in four (columns 4 (tid %
+// 8) + 32 i), so the 8 threads of a row read whole 128-byte lines.
+// (part_o and part_lse are not __restrict__ here: their loads must not move
+// across the compiler barriers that fix the issue order.)
+// The four-split path's issue order, per thread (P(c): partials of chunk c,
+// CO_SG * 2 loads for bf16 and CO_SG * 4 for fp32; W(c): W_UV rows of chunk
+// c, CO_W_LOADS direct loads):
+//   bf16:  log-sum-exps, P(0), W(0), P(1), W(1), P(2), W(2), P(3), W(3)
+//   fp32:  log-sum-exps, P(0), W(0), P(1), W(1), W(2), W(3); P(2) after the
+//          merge of chunk 0 and P(3) after the merge of chunk 1
+// co_after() is the number of loads issued after P(kc) (what = 0) or W(kc)
+// (what = 1) by the time chunk kc waits for them; global stores issued in
+// between only make such a wait stricter.
+constexpr int co_after(bool pb16, int what, int kc) {
+  if (pb16) return (CO_NKC - 1 - kc) * (CO_SG * 2 + CO_W_LOADS) + (what == 0 ? CO_W_LOADS : 0);
+  constexpr int P = CO_SG * 4, Wl = CO_W_LOADS;
+  if (what == 0) return kc == 0 ? Wl + P + 3 * Wl : kc == 1 ? 3 * Wl + P : kc == 2 ? P : 0;
+  // W(2), W(3) precede P(2): once P(2) is in, so are they
+  return kc == 0 ? P + 3 * Wl + P : kc == 1 ? 2 * Wl + 2 * P : kc == 2 ? P : 0;
+}
+
+template <bool PB16, bool OB16>
+__device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, const float* part_lse, int64_t sb,
+                                                int n_split, int s_q, int H, int N, const uint16_t* w_uv,
+                                                uint16_t* out, void* o_lat, float* lse_out) {
+  char* const wt = smem;                               // [4][CO_WBYTES]
+  char* const at = smem + CO_NKC * CO_WBYTES;          // [2 buffers][hi, lo][CF_ABYTES]
+  const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int R = s_q * H;
+  const uint16_t* wsrc = w_uv + (int64_t)h * D_C * D_V;
+
+  constexpr int NL = PB16 ? 2 : 4;           // 16-byte loads per split and chunk
+  constexpr int VW = PB16 ? 8 : 4;           // values per load
+  constexpr int NST = PB16 ? 4 : 2;          // chunks of partials in flight
+  using Raw = typename std::conditional<PB16, u32x4, f32x4>::type;
+  const int r = tid >> 3, cg = tid & 7;
+  const int n = n0 + r;
+  const bool ok = n < N;
+  const int b = ok ? n / s_q : 0;
+  const int row = ok ? (n - b * s_q) * H + h : 0;
+  auto col = [&](int kc, int i) -> int { return kc * CO_KC + (PB16 ? 8 * cg + 64 * i : 4 * cg + 32 * i); };
+  // split s of the group (past the last split: the last one again, weight 0)
+  auto src_row = [&](int s) -> int64_t { return ((sb + max(min(s, n_split - 1), 0)) * R + row) * D_C; };
+  constexpr int LPC = CO_SG * NL;             // loads per chunk of partials
+  u32x4 d[NST][CO_SG][NL];
+  auto load_chunk = [&](int kc, u32x4 (&dst)[CO_SG][NL]) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) ot[8 * (r >> 2) + 4 * half + (r & 3)][v0 + l32] = bf16_bits(to_bf16(acc[r]));
-  __syncthreads();
+    for (int s = 0; s < CO_SG; ++s) {
+      const int64_t base = src_row(s);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int chunk = i * 256 + tid;   // 32 rows x 16 chunks of 16 B
-    const int rr = chunk >> 4, cc = chunk & 15;
-    const int n = n0 + rr;
-    if (n < N) *(i16x8*)(out + ((int64_t)n * H + h) * D_V + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+      for (int i = 0; i < NL; ++i) {
+        if constexpr (PB16) gload_b128(dst[s][i], (const uint16_t*)part_o + base + col(kc, i));
+        else gload_b128(dst[s][i], (const float*)part_o + base + col(kc, i));
+      }
+    }
+  };
+  // issue order (see co_after): the log-sum-exps, then per chunk its
+  // partials (the first NST chunks) and its W_UV rows; the partials of chunk
+  // kc + NST follow the merge of chunk kc
+  float l[CO_SG];
+#pragma unroll
+  for (int s = 0; s < CO_SG; ++s) gload_b32(l[s], part_lse + (sb + max(min(s, n_split - 1), 0)) * R + row);
+  static_for<0, CO_NKC>([&](auto cc) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c < NST) load_chunk(c, d[c]);
+    co_issue_w(wsrc, wt + c * CO_WBYTES, c, wave, lane);
+  });
+  wait_vm<co_after(PB16, 0, 0)>(l[0], l[1], l[2], l[3]);
+
+  // weights of the splits in split order (as the stand-alone merge does)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < CO_SG; ++s) mx = fmaxf(mx, s < n_split ? l[s] : -INFINITY);
+  float w[CO_SG];
+  float wsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < CO_SG; ++s) {
+    w[s] = (s < n_split && l[s] != -INFINITY) ? exp2f(l[s] - mx) : 0.f;
+    if (w[s] != 0.f) wsum += w[s];
   }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  auto vals = [&](const Raw& x, int j) -> f32x4 {
+    if constexpr (PB16) {
+      const uint32_t lo = x[2 * j], hi = x[2 * j + 1];
+      return f32x4{__builtin_bit_cast(float, lo << 16), __builtin_bit_cast(float, lo & 0xFFFF0000u),
+                   __builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xFFFF0000u)};
+    } else {
+      return x;
+    }
+  };
+
+  const int v0 = wave * 32;
+  const int grp = (lane >> 4) & 1, jj = lane & 15;
+  const int bcol = v0 + grp * 16 + 4 * (jj & 3);
+  f32x16 acc_o = f32x16{};
+  static_for<0, CO_NKC>([&](auto kcc) {
+    constexpr int kc = decltype(kcc)::value;
+    constexpr int st = kc % NST;
+    // ---- merge chunk kc, once its loads are in
+    wait_vm<co_after(PB16, 0, kc)>();
+#pragma unroll
+    for (int s = 0; s < CO_SG; ++s)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) touch_reg(d[st][s][i]);
+    f32x4 acc[NL][VW / 4];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int j = 0; j < VW / 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // an absent or empty split (weight 0) may hold anything: its values are
+    // replaced by zeros, which leaves every sum exactly as skipping it does
+#pragma unroll
+    for (int s = 0; s < CO_SG; ++s) {
+      const bool use = w[s] != 0.f;
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < VW / 4; ++j) {
+          const f32x4 x = vals(__builtin_bit_cast(Raw, d[st][s][i]), j);
+          acc[i][j] += w[s] * f32x4{use ? x[0] : 0.f, use ? x[1] : 0.f, use ? x[2] : 0.f, use ? x[3] : 0.f};
+        }
+    }
+    // the registers of chunk kc are free: the partials of chunk kc + NST
+    if constexpr (kc + NST < CO_NKC) load_chunk(kc + NST, d[st]);
+    f32x4 v[NL][VW / 4];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int j = 0; j < VW / 4; ++j) {
+        v[i][j] = acc[i][j] * inv;
+        if (!ok) v[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    // ---- stage the high (+ low) operand planes of the chunk
+    char* const ahi_p = at + (kc & 1) * 2 * CF_ABYTES;
+    char* const alo_p = ahi_p + CF_ABYTES;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+      for (int j = 0; j < VW / 4; ++j) {
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const __bf16 bh = to_bf16(v[i][j][e]);
+          hi[e] = bf16_bits(bh);
+          lo[e] = OB16 ? (uint16_t)0 : bf16_bits(to_bf16(v[i][j][e] - (float)bh));
+        }
+        const uint64_t ph = (uint64_t)hi[0] | ((uint64_t)hi[1] << 16) | ((uint64_t)hi[2] << 32) | ((uint64_t)hi[3] << 48);
+        const uint64_t pl = (uint64_t)lo[0] | ((uint64_t)lo[1] << 16) | ((uint64_t)lo[2] << 32) | ((uint64_t)lo[3] << 48);
+        const int c = col(0, i) + 4 * j;                 // column within the chunk
+        const uint32_t off = cf_aoff(r, c >> 3) + (c & 7) * 2;
+        *(uint64_t*)(ahi_p + off) = ph;
+        *(uint64_t*)(alo_p + off) = pl;
+      }
+    wait_vm<co_after(PB16, 1, kc)>();   // W_UV rows of chunk kc landed (this thread's share)
+    barrier_lds();     // chunk kc's operands visible; the buffer of chunk kc - 2 consumed
+    // the latent output, when asked for (stores issued after the W_UV wait)
+    if (ok && o_lat != nullptr) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int j = 0; j < VW / 4; ++j)
+          part_store(o_lat, ((int64_t)n * H + h) * D_C + col(kc, i) + 4 * j, v[i][j], OB16);
+    }
+    // ---- projection of chunk kc.  The operand reads are inline asm with
+    // exact lgkmcnt waits, one k-step ahead (compiler-issued LDS reads would
+    // first wait for every outstanding global load).
+    {
+      const uint32_t a_base = lds_addr(ahi_p);
+      const uint32_t w_base = lds_addr(wt + kc * CO_WBYTES);
+      // rows 16 ks + 8 half + jj / 4 (+ 4): the XOR of aq_off depends on
+      // the row's low three bits only, so the k-steps are immediate offsets
+      const uint32_t b0 = w_base + aq_off(8 * half + (jj >> 2), bcol);
+      const uint32_t b1 = w_base + aq_off(8 * half + (jj >> 2) + 4, bcol);
+      constexpr int RPK = OB16 ? 3 : 4;              // LDS reads per k-step
+      i16x8 ah[2], al[2];
+      i16x4 bt[2][2];
+      auto issue = [&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        const uint32_t aa = a_base + cf_aoff(l32, 2 * ks + half);
+        lds_read_b128<0>(ah[ks & 1], aa);
+        if constexpr (!OB16) lds_read_b128<CF_ABYTES>(al[ks & 1], aa);
+        lds_read_tr16<ks * 4096>(bt[ks & 1][0], b0);
+        lds_read_tr16<ks * 4096>(bt[ks & 1][1], b1);
+      };
+      issue(std::integral_constant<int, 0>{});
+      static_for<0, CO_KC / 16>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        if constexpr (ks + 1 < CO_KC / 16) issue(std::integral_constant<int, ks + 1>{});
+        constexpr int younger = ks + 1 < CO_KC / 16 ? RPK : 0;
+        wait_lgkm<younger>(ah[ks & 1], al[ks & 1], bt[ks & 1][0], bt[ks & 1][1]);
+        const bf16x8 bw = join_tr(bt[ks & 1][0], bt[ks & 1][1]);
+        acc_o = mfma32(__builtin_bit_cast(bf16x8, ah[ks & 1]), bw, acc_o);
+        if constexpr (!OB16) acc_o = mfma32(__builtin_bit_cast(bf16x8, al[ks & 1]), bw, acc_o);
+      });
+    }
+  });
+  if (ok && lse_out != nullptr && cg == 0)
+    lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
+  // chunk 2's operand buffer is free once every wave is past the last barrier
+  co_store_out(acc_o, at, out, n0, N, H, h, tid, wave, half, l32);
+}
+
+template <bool PB16, bool OB16>
+__global__ __launch_bounds__(256) void combine_out_kernel(const void* part_o, const float* part_lse,
+                                                          const int32_t* __restrict__ seg_first,
+                                                          const int32_t* __restrict__ seg_count,
+                                                          int s_q, int H, int N,
+                                                          const uint16_t* __restrict__ w_uv,
+                                                          uint16_t* __restrict__ out, void* o_lat,
+                                                          float* lse_out) {
+  __shared__ __attribute__((aligned(1024))) char smem[CO_LDS];
+  int* const nmax = (int*)smem;   // read before either path writes the LDS
+  const int n0 = blockIdx.y * CO_ROWS;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // split count and first slot of this thread's row (the four-split path's
+  // row mapping), and the largest split count of the work-group's rows
+  const int r = tid >> 3;
+  const int n = n0 + r;
+  const int b = n < N ? n / s_q : 0;
+  const int64_t sb = seg_first[b];
+  const int ns = seg_count[b];
+  int m = n < N ? ns : 0;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
+  if (lane == 0) nmax[wave] = m;
+  __syncthreads();
+  const int most = max(max(nmax[0], nmax[1]), max(nmax[2], nmax[3]));   // uniform
+  __syncthreads();
+  if (most <= CO_SG)
+    combine_out_few<PB16, OB16>(smem, part_o, part_lse, sb, ns, s_q, H, N, w_uv, out, o_lat, lse_out);
+  else
+    combine_out_many<PB16>(smem, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat, OB16 ? 1 : 0,
+                           lse_out);
 }
 
 }  // namespace
@@ -455,12 +746,17 @@ hipError_t launch_combine_out(const void* part_o, int part_bf16, const float* pa
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
   const int N = B * s_q;
   const dim3 grid(H, (N + CO_ROWS - 1) / CO_ROWS);
-  if (part_bf16)
-    hipLaunchKernelGGL(combine_out_kernel<true>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count,
-                       s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
-  else
-    hipLaunchKernelGGL(combine_out_kernel<false>, grid, dim3(256), 0, stream, part_o, part_lse, seg_first,
-                       seg_count, s_q, H, N, w_uv, out, o_lat, o_bf16, lse);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out,
+                       o_lat, lse);
+  };
+  if (part_bf16) {
+    if (o_bf16) go(combine_out_kernel<true, true>);
+    else go(combine_out_kernel<true, false>);
+  } else {
+    if (o_bf16) go(combine_out_kernel<false, true>);
+    else go(combine_out_kernel<false, false>);
+  }
   return hipGetLastError();
 }
 
