@@ -87,21 +87,26 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
   const int c0 = wave * 32;
   const int grp = (lane >> 4) & 1, jj = lane & 15;
   const int bcol = c0 + grp * 16 + 4 * (jj & 3);
+  // the transposed product, D^T[column][token] (the weight fragment as the
+  // A operand): lane (l32, half) then holds columns 8 g + 4 half .. + 3
+  // (g = 0..3) of token l32, four 8-byte runs of its output row
   f32x16 acc0 = f32x16{}, acc1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < D_NOPE / 16; ++ks) {
     const int krow = ks * 16 + 8 * half + (jj >> 2);
     const bf16x8 bw = join_tr(ds_read_tr16(wt + aq_off(krow, bcol)), ds_read_tr16(wt + aq_off(krow + 4, bcol)));
     const i16x8 z = i16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    acc0 = mfma32(__builtin_bit_cast(bf16x8, ok0 ? a0[ks] : z), bw, acc0);
-    acc1 = mfma32(__builtin_bit_cast(bf16x8, ok1 ? a1[ks] : z), bw, acc1);
+    acc0 = mfma32(bw, __builtin_bit_cast(bf16x8, ok0 ? a0[ks] : z), acc0);
+    acc1 = mfma32(bw, __builtin_bit_cast(bf16x8, ok1 ? a1[ks] : z), acc1);
   }
-  // stage the 64 x 128 output block in LDS, then write whole 256-byte rows
+  // stage the 64 x 128 output block in LDS (8-byte runs), then write whole
+  // 256-byte rows
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = 8 * (r >> 2) + 4 * half + (r & 3);
-    ot[row][c0 + l32] = bf16_bits(to_bf16(acc0[r]));
-    ot[row + 32][c0 + l32] = bf16_bits(to_bf16(acc1[r]));
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int col = c0 + 8 * g4 + 4 * half;
+    *(uint64_t*)&ot[l32][col] = pack_bf16x4(f32x4{acc0[4 * g4], acc0[4 * g4 + 1], acc0[4 * g4 + 2], acc0[4 * g4 + 3]});
+    *(uint64_t*)&ot[l32 + 32][col] =
+        pack_bf16x4(f32x4{acc1[4 * g4], acc1[4 * g4 + 1], acc1[4 * g4 + 2], acc1[4 * g4 + 3]});
   }
   __syncthreads();
 #pragma unroll
