@@ -260,6 +260,8 @@ __global__ __launch_bounds__(256) void absorb_out_kernel(const void* __restrict_
 //    then projected through W_UV in four staged chunks.
 // ---------------------------------------------------------------------------
 constexpr int CO_ROWS = 32;
+constexpr int CO_ROWS_NARROW = 8;                 // rows per work-group of a narrow launch
+constexpr int kComputeUnits = 256;
 constexpr int CO_KC = 128;                        // W_UV rows (latent columns) per chunk
 constexpr int CO_NKC = D_C / CO_KC;               // 4 chunks
 constexpr int CO_WBYTES = CO_KC * D_V * 2;        // 32 KB: W_UV rows of one chunk
@@ -317,7 +319,8 @@ __device__ __forceinline__ void wait_vm(R&... regs) {
 }
 
 // the 32 x 128 output block of the work-group: staged in LDS (wave w wrote
-// its columns), then written as whole 256-byte rows
+// its columns), then its first ROWS rows written as whole 256-byte rows
+template <int ROWS>
 __device__ __forceinline__ void co_store_out(const f32x16& acc, char* stage, uint16_t* out, int n0, int N, int H,
                                              int h, int tid, int wave, int half, int l32) {
   uint16_t(*ot)[D_V + 8] = (uint16_t(*)[D_V + 8])stage;
@@ -330,14 +333,16 @@ __device__ __forceinline__ void co_store_out(const f32x16& acc, char* stage, uin
     const int chunk = i * 256 + tid;   // 32 rows x 16 chunks of 16 B
     const int rr = chunk >> 4, cc = chunk & 15;
     const int n = n0 + rr;
-    if (n < N) *(i16x8*)(out + ((int64_t)n * H + h) * D_V + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+    if (rr < ROWS && n < N) *(i16x8*)(out + ((int64_t)n * H + h) * D_V + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
   }
 }
 
 // Many splits per row: merge all 512 columns (four splits at a time), stage
 // them as bf16 high + low operands in LDS, then stream W_UV[h] through LDS in
-// four 128-row chunks.
-template <bool PB16>
+// four 128-row chunks.  ROWS query rows per work-group (32, or 8 when the
+// launch would otherwise leave compute units idle); the products of the
+// 32-row MFMA tile past them are computed and not stored.
+template <bool PB16, int ROWS>
 __device__ __forceinline__ void combine_out_many(char* smem, const void* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ seg_first,
@@ -346,7 +351,7 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
                                                  void* o_lat, int o_bf16, float* lse_out) {
   char* const wt = smem;                              // [3][CO_WBYTES]: W_UV chunks 0-2, then 3 in slot 0
   char* const at = smem + 3 * CO_WBYTES;              // [2][CO_ABYTES]: [hi, lo]
-  const int h = blockIdx.x, n0 = blockIdx.y * CO_ROWS;
+  const int h = blockIdx.x, n0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
@@ -364,7 +369,7 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
     using Raw = typename std::conditional<PB16, u32x4, f32x4>::type;
     const int r = tid / TPR, cq = (tid % TPR) * VW;
     const int n = n0 + r;
-    const bool ok = r < CO_ROWS && n < N;
+    const bool ok = r < ROWS && n < N;
     const int b = ok ? n / s_q : 0;
     const int row = ok ? (n - b * s_q) * H + h : 0;
     const int64_t sb = seg_first[b];
@@ -417,11 +422,10 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
       for (int j = 0; j < VW / 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < n_split; s0 += CO_SG) {
-      if (s0 > 0) load_group(s0, l, d);
+    auto add_group = [&](int s0, const float (&lg)[CO_SG], const Raw (&dg)[CO_SG][NCH]) {
       float w[CO_SG];
 #pragma unroll
-      for (int u = 0; u < CO_SG; ++u) w[u] = (s0 + u < n_split && l[u] != -INFINITY) ? exp2f(l[u] - mx) : 0.f;
+      for (int u = 0; u < CO_SG; ++u) w[u] = (s0 + u < n_split && lg[u] != -INFINITY) ? exp2f(lg[u] - mx) : 0.f;
 #pragma unroll
       for (int u = 0; u < CO_SG; ++u) {
         if (w[u] == 0.f) continue;      // absent or empty split: its partial may hold anything
@@ -429,11 +433,29 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
 #pragma unroll
         for (int i = 0; i < NCH; ++i)
 #pragma unroll
-          for (int j = 0; j < VW / 4; ++j) acc[i][j] += w[u] * vals(d[u][i], j);
+          for (int j = 0; j < VW / 4; ++j) acc[i][j] += w[u] * vals(dg[u][i], j);
+      }
+    };
+    if constexpr (PB16) {
+      // groups in pairs: the next group's loads are in flight while the
+      // current one is added (two register buffers, so both stay static)
+      float l2[CO_SG];
+      Raw d2[CO_SG][NCH];
+      for (int s0 = 0; s0 < n_split; s0 += 2 * CO_SG) {
+        if (s0 + CO_SG < n_split) load_group(s0 + CO_SG, l2, d2);
+        add_group(s0, l, d);
+        if (s0 + 2 * CO_SG < n_split) load_group(s0 + 2 * CO_SG, l, d);
+        if (s0 + CO_SG < n_split) add_group(s0 + CO_SG, l2, d2);
+      }
+    } else {
+      // fp32 partials: one group's registers are all there is room for
+      for (int s0 = 0; s0 < n_split; s0 += CO_SG) {
+        if (s0 > 0) load_group(s0, l, d);
+        add_group(s0, l, d);
       }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    if (r >= CO_ROWS) return;
+    if (r >= ROWS) return;
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
 #pragma unroll
@@ -463,7 +485,7 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
       lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
   };
   {
-    const int rows_here = min(CO_ROWS, N - n0);
+    const int rows_here = min(ROWS, N - n0);
     if (rows_here > 16) merge(std::integral_constant<int, 8>{});
     else if (rows_here > 8) merge(std::integral_constant<int, 16>{});
     else merge(std::integral_constant<int, 32>{});
@@ -499,7 +521,7 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
     }
   }
   __syncthreads();
-  co_store_out(acc, at, out, n0, N, H, h, tid, wave, half, l32);
+  co_store_out<ROWS>(acc, at, out, n0, N, H, h, tid, wave, half, l32);
 }
 
 // At most four splits per row: W_UV[h] resident in LDS, the partials of the
@@ -707,10 +729,10 @@ __device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, 
   if (ok && lse_out != nullptr && cg == 0)
     lse_out[(int64_t)n * H + h] = wsum > 0.f ? (mx + log2f(wsum)) * 0.69314718055994530942f : -INFINITY;
   // chunk 2's operand buffer is free once every wave is past the last barrier
-  co_store_out(acc_o, at, out, n0, N, H, h, tid, wave, half, l32);
+  co_store_out<CO_ROWS>(acc_o, at, out, n0, N, H, h, tid, wave, half, l32);
 }
 
-template <bool PB16, bool OB16>
+template <bool PB16, bool OB16, int ROWS>
 __global__ __launch_bounds__(256) void combine_out_kernel(const void* part_o, const float* part_lse,
                                                           const int32_t* __restrict__ seg_first,
                                                           const int32_t* __restrict__ seg_count,
@@ -720,7 +742,7 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* part_o, co
                                                           float* lse_out) {
   __shared__ __attribute__((aligned(1024))) char smem[CO_LDS];
   int* const nmax = (int*)smem;   // read before either path writes the LDS
-  const int n0 = blockIdx.y * CO_ROWS;
+  const int n0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // split count and first slot of this thread's row (the four-split path's
@@ -730,18 +752,18 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* part_o, co
   const int b = n < N ? n / s_q : 0;
   const int64_t sb = seg_first[b];
   const int ns = seg_count[b];
-  int m = n < N ? ns : 0;
+  int m = (r < ROWS && n < N) ? ns : 0;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
   if (lane == 0) nmax[wave] = m;
   __syncthreads();
   const int most = max(max(nmax[0], nmax[1]), max(nmax[2], nmax[3]));   // uniform
   __syncthreads();
-  if (most <= CO_SG)
+  if (ROWS == CO_ROWS && most <= CO_SG)
     combine_out_few<PB16, OB16>(smem, part_o, part_lse, sb, ns, s_q, H, N, w_uv, out, o_lat, lse_out);
   else
-    combine_out_many<PB16>(smem, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat, OB16 ? 1 : 0,
-                           lse_out);
+    combine_out_many<PB16, ROWS>(smem, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat,
+                                 OB16 ? 1 : 0, lse_out);
 }
 
 }  // namespace
@@ -750,18 +772,27 @@ hipError_t launch_combine_out(const void* part_o, int part_bf16, const float* pa
                               const int32_t* seg_count, int B, int s_q, int H, const uint16_t* w_uv,
                               uint16_t* out, void* o_lat, int o_bf16, float* lse, hipStream_t stream) {
   const int N = B * s_q;
-  const dim3 grid(H, (N + CO_ROWS - 1) / CO_ROWS);
+  // 32 query rows per work-group, or 8 when that leaves compute units idle
+  // (few query tokens: each work-group then streams a quarter of the rows)
+  const bool narrow = (int64_t)H * ((N + CO_ROWS - 1) / CO_ROWS) < kComputeUnits;
+  const int rows = narrow ? CO_ROWS_NARROW : CO_ROWS;
+  const dim3 grid(H, (N + rows - 1) / rows);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out,
                        o_lat, lse);
   };
-  if (part_bf16) {
-    if (o_bf16) go(combine_out_kernel<true, true>);
-    else go(combine_out_kernel<true, false>);
-  } else {
-    if (o_bf16) go(combine_out_kernel<false, true>);
-    else go(combine_out_kernel<false, false>);
-  }
+  auto pick = [&](auto rc) {
+    constexpr int R = decltype(rc)::value;
+    if (part_bf16) {
+      if (o_bf16) go(combine_out_kernel<true, true, R>);
+      else go(combine_out_kernel<true, false, R>);
+    } else {
+      if (o_bf16) go(combine_out_kernel<false, true, R>);
+      else go(combine_out_kernel<false, false, R>);
+    }
+  };
+  if (narrow) pick(std::integral_constant<int, CO_ROWS_NARROW>{});
+  else pick(std::integral_constant<int, CO_ROWS>{});
   return hipGetLastError();
 }
 
