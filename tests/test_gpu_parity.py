@@ -125,6 +125,13 @@ def small(kind, **kw):
         fp8=W.Workload("fp8", B=2, H=128, s_q=2, causal=True, T=333, cache_dtype="fp8", T_stride=350, seed=55),
         fp8_paged=W.Workload("fp8_paged", B=3, H=64, s_q=1, causal=False, T_range=(60, 300), paged=True,
                              cache_dtype="fp8", seed=56),
+        # enough query rows for the merge + projection to run on 32-row blocks
+        # (H x ceil(N / 32) >= 256 work-groups), the second block partial (N =
+        # 40): three parts per sequence (the four-split path), seven (the
+        # many-split path), and four query tokens per sequence
+        wide=W.Workload("wide", B=40, H=128, s_q=1, causal=False, T=150, seed=57),
+        wide_many=W.Workload("wide_many", B=40, H=128, s_q=1, causal=False, T=600, seed=58),
+        wide_verify=W.Workload("wide_verify", B=10, H=128, s_q=4, causal=True, T=100, seed=59),
     )[kind]
     return base.with_(**kw) if kw else base
 
@@ -197,13 +204,16 @@ def test_split_count_invariance_and_determinism(mla, kind):
     np.testing.assert_array_equal(_f64(out2), results[0][1])
 
 
-@pytest.mark.parametrize("kind", ["contig", "tiny", "verify", "verify_h", "groups_ragged", "paged", "fp8"])
+@pytest.mark.parametrize("kind", ["contig", "tiny", "verify", "verify_h", "groups_ragged", "paged", "fp8",
+                                  "wide", "wide_many", "wide_verify"])
 @pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("part", [torch.float32, torch.bfloat16])
 def test_combine_out_equals_separate_steps(mla, kind, o_dtype, part):
     """The fused merge + projection gives the bits of the merge followed by
     the projection, with and without writing o_lat and lse, for fp32 and
-    bf16 split partials."""
+    bf16 split partials, on each of its paths: 8-row blocks (the small
+    kinds), 32-row blocks with at most four parts per sequence (wide,
+    wide_verify) and with more (wide_many)."""
     w = small(kind)
     inp = W.generate(w)
     q, w_uk, w_uv, cache = W.to_torch(inp)
