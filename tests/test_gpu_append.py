@@ -226,3 +226,26 @@ def test_append_full_size(mla):
     exact = A.append_rows(x, w, inp["pos"], BASE)
     slots = np.array([_slot_of(table, wl.T_cap, int(b), int(p)) for b, p in zip(inp["seq_id"], inp["pos"])])
     _check(rows[slots], scale[slots], exact, _bounds(x, w, wl.d_model), True, "full size")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_append_many_token_blocks(mla, fp8):
+    """16384 + 37 tokens (257 blocks of 64, the last one partial) into a
+    paged cache: every row against the oracle, no other slot touched."""
+    N, d, B, T_cap = 16384 + 37, 128, 8, 4096
+    wl = W.AppendWorkload("t", N=N, d_model=d, B=B, T_cap=T_cap, paged=True,
+                          cache_dtype="fp8" if fp8 else "bf16", seed=400 + int(fp8))
+    inp = W.generate_append(wl)
+    print(f"[append] many token blocks N={N} fp8={fp8}", flush=True)
+    cache, table = _make_cache(mla, B, T_cap, True, fp8, seed=401)
+    before_rows, before_scale = _snapshot(cache)
+    _run(mla, inp["x"], inp["w_dkr"], inp["seq_id"], inp["pos"], cache)
+    rows, scale = _snapshot(cache)
+    x = O.bf16_to_f64(inp["x"])
+    w = O.bf16_to_f64(inp["w_dkr"])
+    exact = A.append_rows(x, w, inp["pos"], BASE)
+    slots = np.array([_slot_of(table, T_cap, int(b), int(p)) for b, p in zip(inp["seq_id"], inp["pos"])])
+    _check(rows[slots], None if not fp8 else scale[slots], exact, _bounds(x, w, d), fp8, "many token blocks")
+    keep = np.ones(len(rows), bool)
+    keep[slots] = False
+    np.testing.assert_array_equal(rows[keep], before_rows[keep])
