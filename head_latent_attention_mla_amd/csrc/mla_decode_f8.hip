@@ -178,17 +178,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     return (int64_t)b * p.T_stride + ts;
   };
   const int soff = wave * (16 * ROWW);
-  auto issue_tile = [&](int tile, int buf) {
+  // the buffer window of a tile; past the last tile an empty window, so its
+  // loads fetch nothing (they write zeros into the idle buffer)
+  auto tile_rsrc = [&](int tile, bool real) {
     const int ts = t_begin + tile * KT;
-    const int valid = __builtin_amdgcn_readfirstlane(min(KT, T - ts));
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(rows + tile_base(tile) * ROWW), (short)0,
-                                                        valid * ROWW, 0x00020000);
+    const int valid = real ? __builtin_amdgcn_readfirstlane(min(KT, T - ts)) : 0;
+    const int64_t base = real ? tile_base(tile) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(rows + base * ROWW), (short)0, valid * ROWW, 0x00020000);
+  };
+  auto issue_load = [&](__amdgpu_buffer_rsrc_t rsrc, int buf, auto kc) {   // load k of this wave's nine
+    constexpr int k = decltype(kc)::value;
+    const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
     char* dst = smem + buf * STAGE + wave * (16 * ROWW);
-    static_for<0, 9>([&](auto kc) {
-      constexpr int k = decltype(kc)::value;
-      const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + k * 1024), 16, vo, soff, 0, 0);
-    });
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + k * 1024), 16, vo, soff, 0, 0);
+  };
+  auto issue_tile = [&](int tile, int buf) {
+    const auto rsrc = tile_rsrc(tile, true);
+    static_for<0, 9>([&](auto kc) { issue_load(rsrc, buf, kc); });
   };
   auto load_scale = [&](int tile) -> float {   // threads 0..63: the scale of tile row tid
     const int ts = t_begin + tile * KT;
@@ -244,10 +250,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
   for (int tile = 0; tile < n_tiles; ++tile) {
     barrier_tile_ready();   // codes and scales of this tile in LDS; the other buffers are free
     const bool has_next = tile + 1 < n_tiles;
-    if (has_next) {
-      issue_tile(tile + 1, (tile + 1) & 1);
-      sc_next = load_scale(tile + 1);
-    }
+    // the next tile's scales now, its codes one load per score k-step below
+    // (a burst of direct loads stalls the issuing wave)
+    if (has_next) sc_next = load_scale(tile + 1);
+    const auto next = tile_rsrc(tile + 1, has_next);
+    const int next_buf = (tile + 1) & 1;
     const uint32_t tb = smem_a + (tile & 1) * STAGE;
     const float* sct = scl + (tile & 1) * 2 * KT;
     const int ts = t_begin + tile * KT;
@@ -308,6 +315,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
         constexpr int NS = ROWW / 64;
         constexpr int ahead = (NS - 1 - ks) < QK_AHEAD ? (NS - 1 - ks) : QK_AHEAD;
         if constexpr (ks + QK_AHEAD < NS) issue_qk(std::integral_constant<int, ks + QK_AHEAD>{});
+        issue_load(next, next_buf, std::integral_constant<int, ks>{});
         constexpr int slot = ks % (QK_AHEAD + 1);
         wait_lgkm<4 * ahead>(ra[slot][0], ra[slot][1], ra[slot][2], ra[slot][3]);
         const u32x4 x0 = __builtin_bit_cast(u32x4, ra[slot][0]), x1 = __builtin_bit_cast(u32x4, ra[slot][1]);
@@ -380,6 +388,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
       // (weights are >= 0), in both lane halves
       pw[0] |= ((kstep & 1) ? 0x80u : 0u) | ((kstep & 2) ? 0x8000u : 0u) | ((kstep & 4) ? 0x800000u : 0u);
     } else {
+      static_for<0, 9>([&](auto kc) { issue_load(next, next_buf, kc); });
 #pragma unroll
       for (int i = 0; i < 8; ++i) pw[i] = 0u;
     }
