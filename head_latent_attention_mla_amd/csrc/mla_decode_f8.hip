@@ -368,10 +368,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
           pb[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x1[4 * gq + i], c_row, nbase));
         }
         const f32x4 sa = sig[0][gq] * sig_w, sbv = sig[1][gq] * sig_w;
-        pw[gq] = e4m3x4(fminf(pa[0] * sa[0], 448.f), fminf(pa[1] * sa[1], 448.f), fminf(pa[2] * sa[2], 448.f),
-                        fminf(pa[3] * sa[3], 448.f));
-        pw[4 + gq] = e4m3x4(fminf(pb[0] * sbv[0], 448.f), fminf(pb[1] * sbv[1], 448.f),
-                            fminf(pb[2] * sbv[2], 448.f), fminf(pb[3] * sbv[3], 448.f));
+        // no clamp to the E4M3 maximum is needed: p <= 2^8 (the reference
+        // rule) and sigma 2^-e < 1 (the choice of e), so every weight is <= 256
+        pw[gq] = e4m3x4(pa[0] * sa[0], pa[1] * sa[1], pa[2] * sa[2], pa[3] * sa[3]);
+        pw[4 + gq] = e4m3x4(pb[0] * sbv[0], pb[1] * sbv[1], pb[2] * sbv[2], pb[3] * sbv[3]);
         // the probabilities the value product actually uses: dequant(w8) / sigma
         // (times 2^e, applied to the sum below)
         const f32x4 ra = *(const f32x4*)(sct + KT + 8 * gq + 4 * half);
@@ -419,35 +419,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
       lds_read_b128<rb * 64 * 32>(bq[rb][0], pb_lane);
       lds_read_b128<rb * 64 * 32 + 16>(bq[rb][1], pb_lane);
     });
-    wait_lgkm<0>(bq[0][0], bq[0][1], bq[1][0], bq[1][1], bq[2][0], bq[2][1], bq[3][0], bq[3][1]);
-    {
-      // reference steps of rows 32 rb + l32, from the sign bits of bytes 0..2
-      float alpha[4];
-      bool any_step = false;
+    // row block by row block as its probability fragments land: the reference
+    // step of rows 32 rb + l32 (sign bits of bytes 0..2) rescales that block's
+    // accumulators first, then its four products
+    static_for<0, 4>([&](auto rbc) {
+      constexpr int rb = decltype(rbc)::value;
+      wait_lgkm<2 * (3 - rb)>(bq[rb][0], bq[rb][1]);
+      u32x4 y0 = __builtin_bit_cast(u32x4, bq[rb][0]);
+      const u32x4 y1 = __builtin_bit_cast(u32x4, bq[rb][1]);
+      const uint32_t d0 = y0[0];
+      const int code = (int)(((d0 >> 7) & 1u) | ((d0 >> 14) & 2u) | ((d0 >> 21) & 4u));
+      if (__builtin_amdgcn_ballot_w64(code != 0) != 0) {
+        const float alpha = code == 0 ? 1.0f : (code == 7 ? 0.0f : __builtin_amdgcn_exp2f(-REF_STEP * code));
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const uint32_t d0 = (uint32_t)__builtin_bit_cast(u32x4, bq[rb][0])[0];
-        const int code = (int)(((d0 >> 7) & 1u) | ((d0 >> 14) & 2u) | ((d0 >> 21) & 4u));
-        alpha[rb] = code == 0 ? 1.0f : (code == 7 ? 0.0f : __builtin_amdgcn_exp2f(-REF_STEP * code));
-        any_step |= code != 0;
-        u32x4 v = __builtin_bit_cast(u32x4, bq[rb][0]);
-        v[0] &= 0xFF7F7F7Fu;
-        bq[rb][0] = __builtin_bit_cast(i16x8, v);
+        for (int c2 = 0; c2 < 4; ++c2) scale_acc(acc[c2][rb], alpha);
       }
-      if (__builtin_amdgcn_ballot_w64(any_step) != 0) {
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2)
-#pragma unroll
-          for (int rb = 0; rb < 4; ++rb) scale_acc(acc[c2][rb], alpha[rb]);
-      }
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const u32x4 y0 = __builtin_bit_cast(u32x4, bq[rb][0]), y1 = __builtin_bit_cast(u32x4, bq[rb][1]);
+      y0[0] &= 0xFF7F7F7Fu;
       const v8i bv = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[cb][rb] = mfma8(av[cb], bv, acc[cb][rb]);
-    }
+    });
     // the next tile's scales go to the buffer the previous tile used
     if (has_next && tid < KT) {
       scl[((tile + 1) & 1) * 2 * KT + tid] = sc_next;
