@@ -259,38 +259,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     const float* sct = scl + (tile & 1) * 2 * KT;
     const int ts = t_begin + tile * KT;
 
-    // this lane's 32 row scales (rows 32 sb + 8 gq + 4 h + i) and the tile's
-    // largest, which every lane of every wave derives alike
+    // this lane's 32 row scales (rows 32 sb + 8 gq + 4 h + i): read now, used
+    // after the score products are issued
     f32x4 sig[2][4];
-    float smax = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        sig[sb][gq] = *(const f32x4*)(sct + 32 * sb + 8 * gq + 4 * half);
-        smax = fmaxf(smax, fmaxf(fmaxf(sig[sb][gq][0], sig[sb][gq][1]), fmaxf(sig[sb][gq][2], sig[sb][gq][3])));
-      }
-    smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-    if (smax > 0.f) {
-      const int e_tile = (int)((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 126;   // smax < 2^e_tile
-      const int e_new = __builtin_amdgcn_readfirstlane(max(e_cur, e_tile));
-      if (e_new != e_cur) {
-        if (e_cur != E_NONE) {
-          const float f = __builtin_ldexpf(1.0f, e_cur - e_new);
-#pragma unroll
-          for (int c2 = 0; c2 < 4; ++c2)
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) scale_acc(acc[c2][rb], f);
-        }
-        e_cur = e_new;
-      }
-    }
-    const float sig_w = e_cur == E_NONE ? 0.f : __builtin_ldexpf(1.0f, -e_cur);
+      for (int gq = 0; gq < 4; ++gq) sig[sb][gq] = *(const f32x4*)(sct + 32 * sb + 8 * gq + 4 * half);
 
     // ================= score phase (owned rows) =================
     uint32_t pw[8];                        // this lane's 32 E4M3 weights (fragment bytes)
+    f32x16 s0 = {}, s1 = {};
+    float smax = 0.f;                      // the tile's largest row scale (every lane alike)
     if (wave_on) {
-      f32x16 s0 = {}, s1 = {};
       constexpr int QK_AHEAD = 2;
       i16x8 ra[QK_AHEAD + 1][4];
       auto issue_qk = [&](auto ksc) {
@@ -324,8 +305,42 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
         const v8i a1 = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
         s0 = mfma8(a0, q8[ks], s0);
         s1 = mfma8(a1, q8[ks], s1);
+        // one group of row scales per k-step, between the products
+        if constexpr (ks < 8) {
+          const f32x4 sg = sig[ks >> 2][ks & 3];
+          smax = max3f(smax, max3f(sg[0], sg[1], sg[2]), sg[3]);
+        }
       });
+    } else {
+      static_for<0, 9>([&](auto kc) { issue_load(next, next_buf, kc); });
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          smax = max3f(smax, max3f(sig[sb][gq][0], sig[sb][gq][1], sig[sb][gq][2]), sig[sb][gq][3]);
+    }
 
+    // the exponent e from the tile's largest row scale
+    {
+      smax = max_halves(smax);
+      if (smax > 0.f) {
+        const int e_tile = (int)((__builtin_bit_cast(uint32_t, smax) >> 23) & 0xFF) - 126;   // smax < 2^e_tile
+        const int e_new = __builtin_amdgcn_readfirstlane(max(e_cur, e_tile));
+        if (e_new != e_cur) {
+          if (e_cur != E_NONE) {
+            const float f = __builtin_ldexpf(1.0f, e_cur - e_new);
+#pragma unroll
+            for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+              for (int rb = 0; rb < 4; ++rb) scale_acc(acc[c2][rb], f);
+          }
+          e_cur = e_new;
+        }
+      }
+    }
+    const float sig_w = e_cur == E_NONE ? 0.f : __builtin_ldexpf(1.0f, -e_cur);
+
+    if (wave_on) {
       // scores in the log2 domain before the row constant: x = S8 * sigma
       float x0[16], x1[16];
 #pragma unroll
@@ -358,7 +373,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
       l_sum = kstep == 7 ? 0.f : l_sum * __builtin_amdgcn_exp2f(-REF_STEP * kstep);
       m_ref = (first || kstep == 7) ? mx : m_ref + REF_STEP * kstep;
       const float nbase = (m_ref == -INFINITY) ? 0.f : -m_ref;
-      float lq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         float pa[4], pb[4];
@@ -372,23 +386,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
         // rule) and sigma 2^-e < 1 (the choice of e), so every weight is <= 256
         pw[gq] = e4m3x4(pa[0] * sa[0], pa[1] * sa[1], pa[2] * sa[2], pa[3] * sa[3]);
         pw[4 + gq] = e4m3x4(pb[0] * sbv[0], pb[1] * sbv[1], pb[2] * sbv[2], pb[3] * sbv[3]);
-        // the probabilities the value product actually uses: dequant(w8) / sigma
-        // (times 2^e, applied to the sum below)
-        const f32x4 ra = *(const f32x4*)(sct + KT + 8 * gq + 4 * half);
-        const f32x4 rb = *(const f32x4*)(sct + KT + 32 + 8 * gq + 4 * half);
-        const auto qa0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[gq], false);
-        const auto qa1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[gq], true);
-        const auto qb0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[4 + gq], false);
-        const auto qb1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[4 + gq], true);
-        lq[gq] += ((qa0[0] * ra[0] + qa0[1] * ra[1]) + (qa1[0] * ra[2] + qa1[1] * ra[3])) +
-                  ((qb0[0] * rb[0] + qb0[1] * rb[1]) + (qb1[0] * rb[2] + qb1[1] * rb[3]));
       }
-      l_sum += sum_halves((lq[0] + lq[1]) + (lq[2] + lq[3])) * (e_cur == E_NONE ? 0.f : __builtin_ldexpf(1.0f, e_cur));
+      // (the tile's share of the normaliser is summed in the value phase)
       // the reference step of the row rides in the sign bits of bytes 0..2
       // (weights are >= 0), in both lane halves
       pw[0] |= ((kstep & 1) ? 0x80u : 0u) | ((kstep & 2) ? 0x8000u : 0u) | ((kstep & 4) ? 0x800000u : 0u);
     } else {
-      static_for<0, 9>([&](auto kc) { issue_load(next, next_buf, kc); });
 #pragma unroll
       for (int i = 0; i < 8; ++i) pw[i] = 0u;
     }
@@ -414,6 +417,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
                      tr[cb][2][0], tr[cb][2][1], tr[cb][3][0], tr[cb][3][1]};
     }
     i16x8 bq[4][2];
+    float lq[4];
     static_for<0, 4>([&](auto rbc) {
       constexpr int rb = decltype(rbc)::value;
       lds_read_b128<rb * 64 * 32>(bq[rb][0], pb_lane);
@@ -438,7 +442,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
       const v8i bv = {(int)y0[0], (int)y0[1], (int)y0[2], (int)y0[3], (int)y1[0], (int)y1[1], (int)y1[2], (int)y1[3]};
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[cb][rb] = mfma8(av[cb], bv, acc[cb][rb]);
+      // under the products: this lane's share of the normaliser, the
+      // probabilities the value product actually uses, dequant(w8) / sigma
+      // (times 2^e below), for its weight group rb (the step bits of word 0
+      // masked off)
+      {
+        constexpr int gq = rb;
+        const uint32_t wa = gq == 0 ? (pw[0] & 0xFF7F7F7Fu) : pw[gq];
+        const f32x4 ra = *(const f32x4*)(sct + KT + 8 * gq + 4 * half);
+        const f32x4 rbv = *(const f32x4*)(sct + KT + 32 + 8 * gq + 4 * half);
+        const auto qa0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wa, false);
+        const auto qa1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)wa, true);
+        const auto qb0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[4 + gq], false);
+        const auto qb1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)pw[4 + gq], true);
+        lq[gq] = ((qa0[0] * ra[0] + qa0[1] * ra[1]) + (qa1[0] * ra[2] + qa1[1] * ra[3])) +
+                 ((qb0[0] * rbv[0] + qb0[1] * rbv[1]) + (qb1[0] * rbv[2] + qb1[1] * rbv[3]));
+      }
     });
+    l_sum += sum_halves((lq[0] + lq[1]) + (lq[2] + lq[3])) * (e_cur == E_NONE ? 0.f : __builtin_ldexpf(1.0f, e_cur));
     // the next tile's scales go to the buffer the previous tile used
     if (has_next && tid < KT) {
       scl[((tile + 1) & 1) * 2 * KT + tid] = sc_next;
