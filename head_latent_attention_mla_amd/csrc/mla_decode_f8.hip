@@ -338,7 +338,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
         }
       }
     }
-    const float sig_w = e_cur == E_NONE ? 0.f : __builtin_ldexpf(1.0f, -e_cur);
 
     if (wave_on) {
       // scores in the log2 domain before the row constant: x = S8 * sigma
@@ -360,11 +359,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = 4 * c;
-        float m = max3f(x0[r], x0[r + 1], x0[r + 2]);
-        m = max3f(m, x0[r + 3], x1[r]);
-        mq[c] = max3f(m, x1[r + 1], fmaxf(x1[r + 2], x1[r + 3]));
+        mq[c] = max3f(max3f(x0[r], x0[r + 1], x0[r + 2]), max3f(x0[r + 3], x1[r], x1[r + 1]),
+                      max3f(x1[r + 2], x1[r + 3], x1[r + 3]));
       }
-      const float mx = max_halves(fmaxf(max3f(mq[0], mq[1], mq[2]), mq[3])) * c_row;
+      const float mx = max_halves(max3f(max3f(mq[0], mq[1], mq[2]), mq[3], mq[3])) * c_row;
       m_run = fmaxf(m_run, mx);
       const bool first = m_ref == -INFINITY;
       const float over = (mx - m_ref - REF_STEP) * (1.0f / REF_STEP);
@@ -372,7 +370,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
       const int kstep = kraw > 7 ? 7 : kraw;
       l_sum = kstep == 7 ? 0.f : l_sum * __builtin_amdgcn_exp2f(-REF_STEP * kstep);
       m_ref = (first || kstep == 7) ? mx : m_ref + REF_STEP * kstep;
-      const float nbase = (m_ref == -INFINITY) ? 0.f : -m_ref;
+      // w = p sigma 2^-e: the exact power of two rides in the exponent
+      // (no scale seen yet: every sigma of the tile is 0 and so is every weight)
+      const float nbase = ((m_ref == -INFINITY) ? 0.f : -m_ref) - (e_cur == E_NONE ? 0.f : (float)e_cur);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         float pa[4], pb[4];
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
           pa[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x0[4 * gq + i], c_row, nbase));
           pb[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x1[4 * gq + i], c_row, nbase));
         }
-        const f32x4 sa = sig[0][gq] * sig_w, sbv = sig[1][gq] * sig_w;
+        const f32x4 sa = sig[0][gq], sbv = sig[1][gq];
         // no clamp to the E4M3 maximum is needed: p <= 2^8 (the reference
         // rule) and sigma 2^-e < 1 (the choice of e), so every weight is <= 256
         pw[gq] = e4m3x4(pa[0] * sa[0], pa[1] * sa[1], pa[2] * sa[2], pa[3] * sa[3]);
