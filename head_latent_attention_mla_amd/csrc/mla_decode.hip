@@ -512,11 +512,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int r = 4 * c;
-        float m = max3f(s0[r], s0[r + 1], s0[r + 2]);
-        m = max3f(m, s0[r + 3], s1[r]);
-        mq[c] = max3f(m, s1[r + 1], fmaxf(s1[r + 2], s1[r + 3]));
+        mq[c] = max3f(max3f(s0[r], s0[r + 1], s0[r + 2]), max3f(s0[r + 3], s1[r], s1[r + 1]),
+                      max3f(s1[r + 2], s1[r + 3], s1[r + 3]));
       }
-      const float mraw = fmaxf(max3f(mq[0], mq[1], mq[2]), mq[3]);
+      const float mraw = max3f(max3f(mq[0], mq[1], mq[2]), mq[3], mq[3]);
       const float mx = max_halves(mraw) * p.scale_log2;
       // reference update, branch-free: the first visible scores set it; later
       // it moves up in steps of REF_STEP only when the maximum passes it by more
