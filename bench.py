@@ -29,12 +29,14 @@ sys.path.insert(0, ROOT)
 
 # the split-T kernel's sources: a traffic figure taken with hardware counters
 # holds only for the code it was taken on
-KERNEL_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_decode.hip",
-                  "head_latent_attention_mla_amd/csrc/mla_decode_f8.hip",
-                  "head_latent_attention_mla_amd/csrc/mla_plan.h",
+# the sources of each split-T kernel: a counter summary stays valid while
+# the digest of its kernel's sources is unchanged
+SHARED_SOURCES = ("head_latent_attention_mla_amd/csrc/mla_plan.h",
                   "head_latent_attention_mla_amd/csrc/mla_common.h",
                   "head_latent_attention_mla_amd/csrc/mla_internal.h",
                   "head_latent_attention_mla_amd/csrc/mla_split_store.h")
+KERNEL_SOURCES = {"bf16": ("head_latent_attention_mla_amd/csrc/mla_decode.hip",) + SHARED_SOURCES,
+                  "fp8math": ("head_latent_attention_mla_amd/csrc/mla_decode_f8.hip",) + SHARED_SOURCES}
 COPY_BYTES = 1 << 30         # read (and written) by the copy-kernel calibration run
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
@@ -66,9 +68,11 @@ def algorithmic_counts(B, s_q, H, seqlens, causal, cache_elem_bytes=2, scale_byt
                 bytes_step=by_cache + by_weights + by_q + by_out)
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(kind: str = "bf16") -> str:
+    """Digest of the sources of the split-T kernel: "bf16" (decode_split_kernel,
+    every workload's scan but the FP8-arithmetic one) or "fp8math"."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -84,7 +88,8 @@ def measured_traffic(workload: str):
     text = open(path).read()
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
     d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    if not t or not d or d.group(1) != kernel_source_digest():
+    kind = "fp8math" if workload.endswith("_fp8math") else "bf16"
+    if not t or not d or d.group(1) != kernel_source_digest(kind):
         return None
     return int(t.group(1))
 
@@ -416,10 +421,11 @@ def main():
                     help="calls of the naive expand-then-attend ablation to time (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the known-size copy kernel that scales the HBM byte counters")
-    ap.add_argument("--kernel-digest", action="store_true", help="print the split-T kernel source digest")
+    ap.add_argument("--kernel-digest", action="store_true",
+                    help="print the source digest of the split-T kernel (of the FP8-arithmetic one with --fp8-math)")
     args = ap.parse_args()
     if args.kernel_digest:
-        print(kernel_source_digest())
+        print(kernel_source_digest("fp8math" if args.fp8_math else "bf16"))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
