@@ -342,7 +342,7 @@ __device__ __forceinline__ void co_store_out(const f32x16& acc, char* stage, uin
 // four 128-row chunks.  ROWS query rows per work-group (32, or 8 when the
 // launch would otherwise leave compute units idle); the products of the
 // 32-row MFMA tile past them are computed and not stored.
-template <bool PB16, int ROWS>
+template <bool PB16, int ROWS, bool EARLY_W>
 __device__ __forceinline__ void combine_out_many(char* smem, const void* __restrict__ part_o,
                                                  const float* __restrict__ part_lse,
                                                  const int32_t* __restrict__ seg_first,
@@ -406,7 +406,7 @@ __device__ __forceinline__ void combine_out_many(char* smem, const void* __restr
     load_group(0, l, d);
     // the first three W_UV chunks load behind the first group of partials
     // (so the merge waits only for its own loads) and during the merge
-    co_issue_w(wsrc, wt, 0, wave, lane);
+    if constexpr (!EARLY_W) co_issue_w(wsrc, wt, 0, wave, lane);   // else issued at kernel entry
     co_issue_w(wsrc, wt + CO_WBYTES, 1, wave, lane);
     co_issue_w(wsrc, wt + 2 * CO_WBYTES, 2, wave, lane);
     float mx = -INFINITY;
@@ -548,7 +548,13 @@ constexpr int co_after(bool pb16, int what, int kc) {
   return kc == 0 ? P + 3 * Wl + P : kc == 1 ? 2 * Wl + 2 * P : kc == 2 ? P : 0;
 }
 
-template <bool PB16, bool OB16>
+// the same counts when W_UV chunk 0 was issued before everything else (at
+// kernel entry): only the merge of chunk 0 has its eight loads fewer behind it
+constexpr int co_after_e(bool pb16, bool early_w, int what, int kc) {
+  return (early_w && what == 0 && kc == 0) ? co_after(pb16, 0, 0) - CO_W_LOADS : co_after(pb16, what, kc);
+}
+
+template <bool PB16, bool OB16, bool EARLY_W>
 __device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, const float* part_lse, int64_t sb,
                                                 int n_split, int s_q, int H, int N, const uint16_t* w_uv,
                                                 uint16_t* out, void* o_lat, float* lse_out) {
@@ -595,9 +601,9 @@ __device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, 
   static_for<0, CO_NKC>([&](auto cc) {
     constexpr int c = decltype(cc)::value;
     if constexpr (c < NST) load_chunk(c, d[c]);
-    co_issue_w(wsrc, wt + c * CO_WBYTES, c, wave, lane);
+    if constexpr (!(EARLY_W && c == 0)) co_issue_w(wsrc, wt + c * CO_WBYTES, c, wave, lane);
   });
-  wait_vm<co_after(PB16, 0, 0)>(l[0], l[1], l[2], l[3]);
+  wait_vm<co_after_e(PB16, EARLY_W, 0, 0)>(l[0], l[1], l[2], l[3]);
 
   // weights of the splits in split order (as the stand-alone merge does)
   float mx = -INFINITY;
@@ -629,7 +635,7 @@ __device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, 
     constexpr int kc = decltype(kcc)::value;
     constexpr int st = kc % NST;
     // ---- merge chunk kc, once its loads are in
-    wait_vm<co_after(PB16, 0, kc)>();
+    wait_vm<co_after_e(PB16, EARLY_W, 0, kc)>();
 #pragma unroll
     for (int s = 0; s < CO_SG; ++s)
 #pragma unroll
@@ -683,7 +689,7 @@ __device__ __forceinline__ void combine_out_few(char* smem, const void* part_o, 
         *(uint64_t*)(ahi_p + off) = ph;
         *(uint64_t*)(alo_p + off) = pl;
       }
-    wait_vm<co_after(PB16, 1, kc)>();   // W_UV rows of chunk kc landed (this thread's share)
+    wait_vm<co_after_e(PB16, EARLY_W, 1, kc)>();   // W_UV rows of chunk kc landed (this thread's share)
     barrier_lds();     // chunk kc's operands visible; the buffer of chunk kc - 2 consumed
     // the latent output, when asked for (stores issued after the W_UV wait)
     if (ok && o_lat != nullptr) {
@@ -741,29 +747,38 @@ __global__ __launch_bounds__(256) void combine_out_kernel(const void* part_o, co
                                                           uint16_t* __restrict__ out, void* o_lat,
                                                           float* lse_out) {
   __shared__ __attribute__((aligned(1024))) char smem[CO_LDS];
-  int* const nmax = (int*)smem;   // read before either path writes the LDS
+  // with bf16 partials and 32-row blocks, W_UV chunk 0 (which needs only the
+  // head) loads into its LDS slot during the split bookkeeping's round trip;
+  // both paths keep chunk 0 there
+  constexpr bool EARLY_W = PB16 && ROWS == CO_ROWS;
   const int n0 = blockIdx.y * ROWS;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // split count and first slot of this thread's row (the four-split path's
-  // row mapping), and the largest split count of the work-group's rows
+  // row mapping); lane l % 32 also fetches the split count of row l % 32, so
+  // that every wave sees every count of the work-group's rows itself.
+  // The loads are inline asm, counted past the W_UV loads behind them.
   const int r = tid >> 3;
   const int n = n0 + r;
   const int b = n < N ? n / s_q : 0;
-  const int64_t sb = seg_first[b];
-  const int ns = seg_count[b];
-  int m = (r < ROWS && n < N) ? ns : 0;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
-  if (lane == 0) nmax[wave] = m;
-  __syncthreads();
-  const int most = max(max(nmax[0], nmax[1]), max(nmax[2], nmax[3]));   // uniform
-  __syncthreads();
-  if (ROWS == CO_ROWS && most <= CO_SG)
-    combine_out_few<PB16, OB16>(smem, part_o, part_lse, sb, ns, s_q, H, N, w_uv, out, o_lat, lse_out);
+  const int rl = lane & 31, nl = n0 + rl;
+  const bool okl = rl < ROWS && nl < N;
+  float f_first, f_count, f_rl;
+  gload_b32(f_first, seg_first + b);
+  gload_b32(f_count, seg_count + b);
+  gload_b32(f_rl, seg_count + (okl ? nl / s_q : 0));
+  if constexpr (EARLY_W) co_issue_w(w_uv + (int64_t)blockIdx.x * D_C * D_V, smem, 0, wave, lane);
+  wait_vm<EARLY_W ? CO_W_LOADS : 0>(f_first, f_count, f_rl);
+  const int64_t sb = __builtin_bit_cast(int32_t, f_first);
+  const int ns = __builtin_bit_cast(int32_t, f_count);
+  // a row with more than four splits takes the many-split path (the same
+  // answer in every wave)
+  const bool many = __builtin_amdgcn_ballot_w64(okl && __builtin_bit_cast(int32_t, f_rl) > CO_SG) != 0;
+  if (ROWS == CO_ROWS && !many)
+    combine_out_few<PB16, OB16, EARLY_W>(smem, part_o, part_lse, sb, ns, s_q, H, N, w_uv, out, o_lat, lse_out);
   else
-    combine_out_many<PB16, ROWS>(smem, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out, o_lat,
-                                 OB16 ? 1 : 0, lse_out);
+    combine_out_many<PB16, ROWS, EARLY_W>(smem, part_o, part_lse, seg_first, seg_count, s_q, H, N, w_uv, out,
+                                          o_lat, OB16 ? 1 : 0, lse_out);
 }
 
 }  // namespace
