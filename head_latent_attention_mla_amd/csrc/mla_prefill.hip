@@ -476,14 +476,15 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
         s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
       }
     }
+    // (max3 only: no NaN-quieting moves; scores are finite or -inf)
     float mq[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int r = 4 * c;
-      mq[c] = fmaxf(fmaxf(fmaxf(s0[r], s0[r + 1]), fmaxf(s0[r + 2], s0[r + 3])),
-                    fmaxf(fmaxf(s1[r], s1[r + 1]), fmaxf(s1[r + 2], s1[r + 3])));
+      mq[c] = max3f(max3f(s0[r], s0[r + 1], s0[r + 2]), max3f(s0[r + 3], s1[r], s1[r + 1]),
+                    max3f(s1[r + 2], s1[r + 3], s1[r + 3]));
     }
-    const float mraw = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+    const float mraw = max3f(max3f(mq[0], mq[1], mq[2]), mq[3], mq[3]);
     float ma = mraw, mb = mraw;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(ma), "+v"(mb));
     const float mx = fmaxf(ma, mb) * p.scale_log2;
