@@ -469,11 +469,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillParams p, i
 
     // rows at or past the own limit do not count
     if (__builtin_amdgcn_ballot_w64(ts + KT > lim) != 0) {
+      // row t = ts + 4 half + o (o = 8 (r / 4) + r % 4, + 32 in s1) is
+      // visible when o < lim - ts - 4 half: one distance, constant offsets
+      const int d = lim - ts - 4 * half;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = ts + 8 * (r >> 2) + 4 * half + (r & 3);
-        s0[r] = (t < lim) ? s0[r] : -INFINITY;
-        s1[r] = (t + 32 < lim) ? s1[r] : -INFINITY;
+        const int o = 8 * (r >> 2) + (r & 3);
+        s0[r] = (o < d) ? s0[r] : -INFINITY;
+        s1[r] = (o + 32 < d) ? s1[r] : -INFINITY;
       }
     }
     // (max3 only: no NaN-quieting moves; scores are finite or -inf)
