@@ -81,8 +81,9 @@ __device__ __forceinline__ int opaque(int x) {
 
 // LDS layout.  bf16 cache: two tile buffers (double-buffered loads) + P.
 // FP8 cache: one bf16 tile buffer, two staging buffers for the e4m3 codes
-// (double-buffered loads) + P; each tile is converted codes * row scale ->
-// bf16 into the tile buffer, after which both paths are identical.
+// (double-buffered loads) + P; each tile's codes are decoded exactly to bf16
+// into the tile buffer, and each row's scale is applied outside the products:
+// to the row's scores, and to its probabilities in the value product.
 constexpr int STAGE_BYTES = KT * ROWW;        // 36,864: e4m3 codes of one tile
 static_assert(TILE_BYTES + 2 * STAGE_BYTES == 2 * TILE_BYTES, "layouts share the P offset");
 
@@ -354,8 +355,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     const int ts = t_begin + tile * KT;
     return (ts + cv_row < T) ? p.row_scale[tile_base(tile) + cv_row] : 0.f;
   };
-  // the nine 16-code chunks are read first (one LDS round trip, not nine),
-  // then converted two values per conversion instruction and written
+  // every E4M3 value is a bf16 value: the codes are decoded exactly (gfx950's
+  // scaled conversion with scale 1, two codes per instruction).  The nine
+  // 16-code chunks are read first (one LDS round trip, not nine).  The row's
+  // scale goes to each wave's copy of the tile's 64 scales, at the head of
+  // that wave's probability fragments (idle until the wave writes them).
   auto convert_tile = [&](int buf, float scale) {
     const char* src = smem + TILE_BYTES + buf * STAGE_BYTES + cv_row * ROWW + cv_q * 9 * 16;
     u32x4 w[9];
@@ -364,15 +368,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
 #pragma unroll
     for (int i = 0; i < 9; ++i) {
       const int m = cv_q * 9 + i;                 // 16-code chunk of the row
-      uint64_t o[4];
+      uint32_t o[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i][d], true);
-        o[d] = pack_bf16x4(f32x4{lo[0] * scale, lo[1] * scale, hi[0] * scale, hi[1] * scale});
+        o[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][d], 1.0f, false));
+        o[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i][d], 1.0f, true));
       }
-      *(u32x4*)(smem + lds_off(cv_row, 16 * m)) = u32x4{(uint32_t)o[0], (uint32_t)(o[0] >> 32), (uint32_t)o[1], (uint32_t)(o[1] >> 32)};
-      *(u32x4*)(smem + lds_off(cv_row, 16 * m + 8)) = u32x4{(uint32_t)o[2], (uint32_t)(o[2] >> 32), (uint32_t)o[3], (uint32_t)(o[3] >> 32)};
+      *(u32x4*)(smem + lds_off(cv_row, 16 * m)) = u32x4{o[0], o[1], o[2], o[3]};
+      *(u32x4*)(smem + lds_off(cv_row, 16 * m + 8)) = u32x4{o[4], o[5], o[6], o[7]};
+    }
+    if (cv_q == 0) {
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) *(float*)(pbuf + w2 * 4096 + cv_row * 4) = scale;
     }
   };
 
@@ -444,8 +451,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     const int next_buf = (tile + 1) & 1;
     uint32_t tb_a;
     if constexpr (FP8) {
-      // dequantise the staged codes into the bf16 tile buffer; rows past the
-      // sequence end have scale 0 and become zeros
+      // decode the staged codes into the bf16 tile buffer (rows past the
+      // sequence end load as zero codes and have scale 0)
       sc_cur = sc_next;
       if (has_next) sc_next = load_scale(tile + 1);
       convert_tile(tile & 1, sc_cur);
@@ -496,6 +503,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
         __builtin_amdgcn_sched_barrier(0);   // keep the k-step's waits, reads and MFMAs in order
       });
       mfma_v_drain(s0, s1);
+      // FP8: the scales of the lane's 32 tile rows, 8 (r / 4) + 4 half + r % 4
+      // (group g = r / 4) and 32 more (group 4 + g), read from this wave's
+      // copy four groups at a time
+      const uint32_t scl_a = pbuf_a + wave * 4096 + 16 * half;
+      auto read_scales = [&](f32x4 (&sg)[4], auto g0c) {
+        constexpr int g0 = decltype(g0c)::value;
+        static_for<0, 4>([&](auto gc) {
+          constexpr int g8 = g0 + decltype(gc)::value;
+          i16x8 t;
+          lds_read_b128<32 * g8>(t, scl_a);
+          sg[g8 - g0] = __builtin_bit_cast(f32x4, t);
+        });
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i) touch_reg(sg[i]);
+      };
+      if constexpr (FP8) {
+        f32x4 sg[4];
+        read_scales(sg, std::integral_constant<int, 0>{});
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s0[r] *= sg[r >> 2][r & 3];
+        read_scales(sg, std::integral_constant<int, 4>{});
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s1[r] *= sg[r >> 2][r & 3];
+      }
 
       // mask only where the tile reaches past a row's last visible row
       if (__builtin_amdgcn_ballot_w64(ts + KT > lim) != 0) {
@@ -526,23 +558,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
       l_sum = kstep == 7 ? 0.f : l_sum * __builtin_amdgcn_exp2f(-REF_STEP * kstep);
       m_ref = (first || kstep == 7) ? mx : m_ref + REF_STEP * kstep;
       const float nbase = (m_ref == -INFINITY) ? 0.f : -m_ref;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pk[0][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
-        pk[1][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
-      }
-      // row sum of the rounded probabilities, two at a time in four chains
       float lq[4] = {0.f, 0.f, 0.f, 0.f};
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      if constexpr (FP8) {
+        // value-product weights p * (row scale), rounded to bf16; the
+        // normaliser is the sum of the probabilities themselves
+        f32x4 sg[4];
+        read_scales(sg, std::integral_constant<int, 0>{});
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+        for (int r = 0; r < 16; ++r) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase));
+          lq[r & 3] += e0;
+          pk[0][r >> 3][r & 7] = to_bf16(e0 * sg[r >> 2][r & 3]);
+        }
+        read_scales(sg, std::integral_constant<int, 4>{});
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int r = 0; r < 16; ++r) {
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase));
+          lq[r & 3] += e1;
+          pk[1][r >> 3][r & 7] = to_bf16(e1 * sg[r >> 2][r & 3]);
+        }
+      } else {
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pr = {pk[sb][j][e], pk[sb][j][e + 1]};
-            lq[2 * j + sb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq[2 * j + sb], false);
-          }
+        for (int r = 0; r < 16; ++r) {
+          pk[0][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], p.scale_log2, nbase)));
+          pk[1][r >> 3][r & 7] = to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.scale_log2, nbase)));
+        }
+        // row sum of the rounded probabilities, two at a time in four chains
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const bf16x2 pr = {pk[sb][j][e], pk[sb][j][e + 1]};
+              lq[2 * j + sb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lq[2 * j + sb], false);
+            }
+      }
       l_sum += sum_halves((lq[0] + lq[1]) + (lq[2] + lq[3]));
       if (kstep != 0) {
         // sign bits of the fragment's first three probabilities carry the
