@@ -100,7 +100,10 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     acc1 = mfma32(bw, __builtin_bit_cast(bf16x8, ok1 ? a1[ks] : z), acc1);
   }
   // stage the 64 x 128 output block in LDS (8-byte runs), then write whole
-  // 256-byte rows
+  // 256-byte rows.  The rows are written with the nontemporal hint: they are
+  // read back only by the next kernel, and left as dirty lines in this XCD's
+  // L2 they lengthen the end of the launch (measured: 10.3 -> 9.4 us at
+  // B = 64, H = 128)
 #pragma unroll
   for (int g4 = 0; g4 < 4; ++g4) {
     const int col = c0 + 8 * g4 + 4 * half;
@@ -115,14 +118,15 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const uint16_t* __restric
     const int rr = chunk >> 4, cc = chunk & 15;
     const int nn = n0 + rr;
     if (nn < N)
-      *(i16x8*)(q_lat + ((int64_t)nn * H + h) * ROWW + cblk * AQ_COLS + cc * 8) = *(const i16x8*)&ot[rr][cc * 8];
+      __builtin_nontemporal_store(*(const i16x8*)&ot[rr][cc * 8],
+                                  (i16x8*)(q_lat + ((int64_t)nn * H + h) * ROWW + cblk * AQ_COLS + cc * 8));
   }
   // the rope part of the query rows is carried over unchanged
   if (rope_on) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int n = n0 + rr0 + 32 * i;
-      if (n < N) *(i16x8*)(q_lat + ((int64_t)n * H + h) * ROWW + D_C + rc * 8) = rope[i];
+      if (n < N) __builtin_nontemporal_store(rope[i], (i16x8*)(q_lat + ((int64_t)n * H + h) * ROWW + D_C + rc * 8));
     }
   }
 }
