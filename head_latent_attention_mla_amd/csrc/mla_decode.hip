@@ -324,7 +324,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     if constexpr (FP8) {
       // 16 rows of codes are 9 KB contiguous: plain lane order into staging
       char* dst = smem + TILE_BYTES + buf * STAGE_BYTES + wave * (16 * ROWW) + k * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0,
+                                               CPOL_STREAM);
     } else {
       constexpr int k9 = k % 9;
       const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
@@ -336,10 +337,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
         constexpr int r = a + (k >= 9 ? 8 : 0);
         uint32_t row_adj = adj[r];
         if constexpr (split < 64) row_adj = lane < split ? adj[r] : adj[r + 1];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo + row_adj, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo + row_adj, 0, 0, CPOL_STREAM);
       } else {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, vo,
-                                                 soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, 0);
+                                                 soff + (k >= 9 ? 8 * ROWW * 2 : 0), 0, CPOL_STREAM);
       }
     }
   };
