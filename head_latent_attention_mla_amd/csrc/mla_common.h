@@ -20,11 +20,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-// Cache-policy operand of the direct-to-LDS tile loads of the latent scans:
-// the nontemporal (streaming) bit of the gfx950 memory instructions.  A scan
-// reads each cached row once per work-group, so the lines are marked for
-// early eviction and the data that is read again (the latent queries, the
-// absorption weights of the next step) stays in the caches.
+// Cache-policy operand of the direct-to-LDS tile loads of the bf16 latent
+// scans: the nontemporal (streaming) bit of the gfx950 memory instructions.
+// A scan reads each cached row once per work-group, so the lines are marked
+// for early eviction and the data that is read again (the latent queries, the
+// absorption weights of the next step) stays in the caches.  The E4M3 scans
+// keep the default policy: their query-row groups read each tile through L2
+// at different times, and with the hint 10-27% more of it came from HBM.
 constexpr int CPOL_STREAM = 2;
 
 // XOR pattern applied to the 16-byte chunk index of LDS row t.  For any 8

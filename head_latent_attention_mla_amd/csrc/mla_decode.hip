@@ -324,8 +324,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_kernel(DecodeParams 
     if constexpr (FP8) {
       // 16 rows of codes are 9 KB contiguous: plain lane order into staging
       char* dst = smem + TILE_BYTES + buf * STAGE_BYTES + wave * (16 * ROWW) + k * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0,
-                                               CPOL_STREAM);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 16, lane * 16, soff + k * 1024, 0, 0);
     } else {
       constexpr int k9 = k % 9;
       const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;

@@ -190,8 +190,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void decode_split_f8_kernel(DecodePara
     constexpr int k = decltype(kc)::value;
     const uint32_t vo = (loff[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
     char* dst = smem + buf * STAGE + wave * (16 * ROWW);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + k * 1024), 16, vo, soff, 0,
-                                             CPOL_STREAM);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(dst + k * 1024), 16, vo, soff, 0, 0);
   };
   auto issue_tile = [&](int tile, int buf) {
     const auto rsrc = tile_rsrc(tile, true);
